@@ -72,13 +72,15 @@ def pack(W, bits: int, group: int = 128):
 
 
 def words(Q_row: list[int], bits: int) -> list[int]:
-    """Pack one row of codes into uint32 words, code k at bits b*(k mod 32/b)."""
+    """Pack one row of codes into uint32 words: code j of a word (j = k mod 32/b)
+    at bit 16*(j mod 2) + b*(j // 2), i.e. even codes in the low half-word and
+    odd codes in the high half-word."""
     per = 32 // bits
     out = []
     for i in range(0, len(Q_row), per):
         w = 0
         for j, q in enumerate(Q_row[i:i + per]):
-            w |= int(q) << (bits * j)
+            w |= int(q) << (16 * (j % 2) + bits * (j // 2))
         out.append(w)
     return out
 

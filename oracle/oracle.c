@@ -25,7 +25,9 @@
  *  - range: lo = min(0, min W), hi = max(0, max W); s = fp16((hi-lo)/(2^b-1)),
  *    s := 1 when it rounds to 0; overflow of s is an error;
  *  - rounding: round-half-to-even everywhere (codes, z, FP16 conversions);
- *  - bit order: code k of a uint32 word sits at bits [b*(k mod 32/b), +b);
+ *  - bit order: code j = k mod (32/b) of a uint32 word sits at bit
+ *    16*(j mod 2) + b*floor(j/2): the even codes fill the low 16 bits and the
+ *    odd codes the high 16 bits, each half from its least significant bit;
  *  - layout: codes [N][K*b/32] uint32, scales/zeros [N][K/G] FP16, N-major;
  *  - glue between the projections: parameter-free LayerNorm (eps 1e-5,
  *    population variance), self-only attention (the V slice of qkv, columns
@@ -101,6 +103,12 @@ uint16_t or_double_to_half_bits(double v)
     return sign | (uint16_t)((E + 15) << 10) | f;
 }
 
+/* Bit position of code j (0 <= j < 32/bits) inside its uint32 word. */
+static int code_shift(int bits, int j)
+{
+    return 16 * (j & 1) + bits * (j >> 1);
+}
+
 /* ---------------------------------------------------------- validation --- */
 
 static int check_format(int32_t bits, int32_t K, int32_t N, int32_t group)
@@ -119,8 +127,8 @@ static int check_format(int32_t bits, int32_t K, int32_t N, int32_t group)
 /* Per (n, group): lo/hi over the group (with 0 included), s = fp16 of the FP64
  * quotient (hi - lo) / (2^b - 1) (CTX-TIER kernel details: scale = range / 3
  * for INT2), integer zero point z = rne(-lo / s), codes q = rne(W / s) + z,
- * both clamped to [0, 2^b - 1], packed b bits at a time from the LSB of each
- * uint32 word along K.  W is FP32 [K][ldw].  Returns OR_EINVAL for non-finite
+ * both clamped to [0, 2^b - 1], packed along K into uint32 words (code j of a
+ * word at bit code_shift(b, j)).  W is FP32 [K][ldw].  Returns OR_EINVAL for non-finite
  * W or a scale that overflows FP16. */
 int or_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits,
             int32_t group, uint32_t* codes, uint16_t* scales, uint16_t* zeros)
@@ -170,7 +178,7 @@ int or_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits,
                 if (q > qmax)
                     q = qmax;
                 codes[(int64_t)n * words_per_row + k / per_word] |=
-                    ((uint32_t)q) << (bits * (k % per_word));
+                    ((uint32_t)q) << code_shift(bits, k % per_word);
             }
         }
     }
@@ -179,7 +187,7 @@ int or_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits,
 
 /* -------------------------------------------------------------- unpack --- */
 
-/* q[n][k] = (codes[n][k / (32/b)] >> (b * (k mod 32/b))) & (2^b - 1). */
+/* q[n][k] = (codes[n][k / (32/b)] >> code_shift(b, k mod 32/b)) & (2^b - 1). */
 int or_unpack(const uint32_t* codes, int32_t K, int32_t N, int32_t bits,
               uint8_t* q)
 {
@@ -192,7 +200,7 @@ int or_unpack(const uint32_t* codes, int32_t K, int32_t N, int32_t bits,
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
             q[n * K + k] = (uint8_t)((codes[n * words_per_row + k / per_word] >>
-                                      (bits * (k % per_word))) & mask);
+                                      code_shift(bits, (int)(k % per_word))) & mask);
     return OR_OK;
 }
 
@@ -210,7 +218,7 @@ static void dequant_row(const uint32_t* codes, const uint16_t* scales,
     const uint32_t mask = (1u << bits) - 1u;
     for (int64_t k = 0; k < K; ++k) {
         uint32_t q = (codes[n * words_per_row + k / per_word] >>
-                      (bits * (k % per_word))) & mask;
+                      code_shift(bits, (int)(k % per_word))) & mask;
         int64_t g = k / group;
         double s = or_half_to_double(scales[n * groups + g]);
         double z = or_half_to_double(zeros[n * groups + g]);

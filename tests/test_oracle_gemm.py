@@ -19,7 +19,7 @@ def _packed(orc, bits, codes_nk, scales, zeros):
     per = 32 // bits
     words = np.zeros((N, K // per), dtype=np.uint64)
     for j in range(per):
-        words |= (codes_nk[:, j::per].astype(np.uint64) << np.uint64(bits * j))
+        words |= (codes_nk[:, j::per].astype(np.uint64) << np.uint64(16 * (j % 2) + bits * (j // 2)))
     s = np.asarray(scales, dtype=np.float64).reshape(N, K // 128)
     z = np.asarray(zeros, dtype=np.float64).reshape(N, K // 128)
     return orc.Packed(bits, K, N, words.astype(np.uint32), orc.half_bits(s), orc.half_bits(z))

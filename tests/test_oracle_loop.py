@@ -32,7 +32,7 @@ def _diag_packed(orc, K, N, value, pairs, bits=4):
     per = 32 // bits
     words = np.zeros((N, K // per), dtype=np.uint64)
     for j in range(per):
-        words |= q[:, j::per].astype(np.uint64) << np.uint64(bits * j)
+        words |= q[:, j::per].astype(np.uint64) << np.uint64(16 * (j % 2) + bits * (j // 2))
     G = K // 128
     return orc.Packed(bits, K, N, words.astype(np.uint32),
                       orc.half_bits(np.full((N, G), value)), orc.half_bits(np.zeros((N, G))))
