@@ -1,0 +1,152 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) weight-only INT4/INT2 quantised GEMM
+ * library (libqgemm.so) and of the looped, weight-shared block that calls it.
+ *
+ * The operation is the quantised linear layer of the TinyLoop runtime
+ * (quant_gemm for INT4 weights, int2_gemm after the CTX-TIER switch to INT2;
+ * "β-Informed Deployment Features" page, CTX-TIER section): FP16 activations
+ * times INT4- or INT2-packed weights that carry one FP16 scale and one FP16
+ * zero per group of 128 weights along K ("Model" page, VRAM cost; CTX-TIER
+ * "Details of the shipped kernel").
+ *
+ * Packed format, layout version 1 (b = bits in {4, 2}, G = 128, g = k / G):
+ *   - codes:  uint32 [N][K*b/32], row n = output channel n, contiguous along K
+ *             (INT4 rows are K/2 bytes, INT2 rows K/4 bytes).  Inside a word,
+ *             code j (j = k mod 32/b) sits at bit 16*(j mod 2) + b*floor(j/2):
+ *             even codes in the low half-word, odd codes in the high half-word.
+ *   - scales: FP16 [N][K/G];  zeros: FP16 [N][K/G], integer values in
+ *             [0, 2^b - 1].
+ *   - dequant: w^[k][n] = (q[n][k] - zeros[n][g]) * scales[n][g].
+ *   - pack of FP32 W [K][N], per (n, g): lo = min(0, min W), hi = max(0, max W),
+ *     s = fp16_rne((hi - lo) / (2^b - 1)) (quotient in FP64; s := 1 if it
+ *     rounds to 0), z = clamp(rne(-lo / s), 0, 2^b - 1),
+ *     q = clamp(rne(W / s) + z, 0, 2^b - 1); rne = round half to even.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or retains them beyond the call (cached launch plans keep
+ *     only their values, see qg_release_cache).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     in stream order and the call returns without synchronising unless the
+ *     entry says otherwise.  Kernel faults surface at the caller's next sync.
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     a non-zero return nothing was enqueued and no output was touched.
+ *     qg_last_error() (thread-local) then names the failed check.
+ *   - Calls on the same outputs/scratch from two streams race; calls on
+ *     distinct buffers may run concurrently.
+ *   - Results are deterministic: the same call on the same inputs gives the
+ *     same bits (no floating-point atomics).
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+#define QG_LAYOUT_VERSION 1
+
+/* Status codes.  EINVAL: bad argument (the pages' ValueError); EUNSUPPORTED:
+ * bits/group outside layout v1; ENOMEM / EHIP: runtime failure (the pages'
+ * RuntimeError, "Model" page, Raises). */
+#define QG_OK 0
+#define QG_EINVAL (-1)
+#define QG_EUNSUPPORTED (-2)
+#define QG_ENOMEM (-3)
+#define QG_EHIP (-4)
+
+typedef uint16_t qg_half; /* IEEE binary16 bit pattern */
+
+/* One packed weight (the pages' QuantWeight: packed data, FP16 scales and
+ * zeros, bits; CTX-TIER Phase 2).  bits in {4, 2}; group == 128; K % 128 == 0;
+ * N >= 1; codes 16-byte aligned; scales/zeros 2-byte aligned. */
+typedef struct qg_weight {
+    int32_t bits;
+    int32_t K;
+    int32_t N;
+    int32_t group;
+    const uint32_t* codes;
+    const qg_half* scales;
+    const qg_half* zeros;
+} qg_weight;
+
+/* The loop block's four projections (CTX-TIER Phase 2b names the block's
+ * attn_qkv, attn_out, mlp_up and mlp_down weights): qkv K=D, N=3D; out K=D,
+ * N=D; up K=D, N=F; down K=F, N=D.  Each weight carries its own bits. */
+typedef struct qg_block {
+    int32_t D;
+    int32_t F;
+    qg_weight qkv;
+    qg_weight out;
+    qg_weight up;
+    qg_weight down;
+} qg_block;
+
+int qg_abi_version(void);
+int qg_layout_version(void);
+/* Message of the last failed call on this thread ("" if none). */
+const char* qg_last_error(void);
+
+/* Quantise FP32 W [K][ldw] (ldw >= N) into layout v1 (see the format above;
+ * CTX-TIER kernel details: per-group asymmetric scale = range / (levels - 1)).
+ * codes [N][K*bits/32], scales and zeros [N][K/128] are written in full.
+ * Bit-identical to the definition (FP64 arithmetic on the device).
+ * Synchronises `stream` before returning, because it reports non-finite W or
+ * a scale that overflows FP16 as QG_EINVAL (outputs are then unspecified). */
+int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int32_t group,
+            uint32_t* codes, qg_half* scales, qg_half* zeros, void* stream);
+
+/* Y[M][N] = X[M][K] . dequant(w)[K][N] (quant_gemm, "β-Informed Deployment
+ * Features" page).  X FP16 [M][ldx], Y FP16 [M][ldy], ldx >= K, ldy >= N, both
+ * multiples of 8 and 16-byte aligned pointers; FP32 accumulation, one
+ * round-to-nearest-even to FP16 at the end.  M == 0 is a no-op.
+ * w->bits must be 4 (qg_gemm_int4) or 2 (qg_gemm_int2), like the pages'
+ * dispatch on QuantWeight::bits.  ws/ws_bytes: device workspace of at least
+ * qg_gemm_ws_bytes(w, M) bytes (may be NULL when that is 0). */
+int qg_gemm_int4(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
+                 int32_t M, void* ws, size_t ws_bytes, void* stream);
+int qg_gemm_int2(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
+                 int32_t M, void* ws, size_t ws_bytes, void* stream);
+size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M);
+
+/* Iterations [L0, L1) of the shared block, in place on the FP32 residual
+ * h [M][D] (run_loop_iters_range, "Warm-start mid-loop" page, internal flow:
+ * the same weights are applied on every iteration).  Per iteration:
+ *   x = fp16(LN(h)); qkv = fp16(x . Wqkv); o = fp16(qkv[:, 2D:3D] . Wout);
+ *   h += o; x = fp16(LN(h)); u = fp16(x . Wup); d = fp16(u . Wdown); h += d;
+ * LN is parameter-free, eps 1e-5, population variance, computed in FP32.
+ * Requires 0 <= L0 <= L1; L0 == L1 (or M == 0) is a no-op.  [L0, L1) followed
+ * by [L1, L2) gives the same bits as [L0, L2).
+ * scratch: device buffer of at least qg_loop_scratch_bytes(blk, M) bytes; after
+ * the call it holds the last iteration's FP16 intermediates at the offsets
+ * given by qg_loop_scratch_offsets (norm = second LN output [M][D],
+ * qkv [M][3D], u [M][F], y = last down-projection output [M][D]). */
+int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
+                  void* scratch, size_t scratch_bytes, void* stream);
+size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M);
+/* Byte offsets of norm, qkv, u and y inside the loop scratch (any pointer may
+ * be NULL).  Returns QG_EINVAL for a bad block. */
+int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t* qkv,
+                            size_t* u, size_t* y);
+
+/* Test exports running the same device unpack/dequant code the GEMM kernels
+ * use.  qg_unpack writes codes q [N][K] as uint8.  qg_dequant writes
+ * w^ [N][K] (N-major) as FP32 when out_fp16 == 0 (exact) or as FP16
+ * (round-to-nearest-even of the exact value) when out_fp16 != 0. */
+int qg_unpack(const qg_weight* w, uint8_t* q, void* stream);
+int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream);
+
+/* Frees library-owned device state (cached launch plans, the pack status
+ * word) after synchronising the device.  Safe to call at any time when no
+ * library call is in flight on another thread. */
+void qg_release_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,267 @@
+"""Python binding of libqgemm.so, the MI355X (gfx950) weight-only INT4/INT2
+quantised GEMM library (C ABI in include/qgemm.h).
+
+Argument marshalling only: every function here takes torch tensors that live
+on the GPU, passes their device pointers and the current HIP stream to the
+C entry point of the same name, and raises on a non-zero status.  No step of
+the computation runs in Python, and there is no CPU fallback: importing the
+package fails loudly when the compiled library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOMEM, QG_EHIP = 0, -1, -2, -3, -4
+GROUP = 128
+
+
+class QGError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class QGValueError(QGError, ValueError):
+    pass
+
+
+class _Weight(C.Structure):
+    _fields_ = [("bits", C.c_int32), ("K", C.c_int32), ("N", C.c_int32), ("group", C.c_int32),
+                ("codes", C.c_void_p), ("scales", C.c_void_p), ("zeros", C.c_void_p)]
+
+
+class _Block(C.Structure):
+    _fields_ = [("D", C.c_int32), ("F", C.c_int32),
+                ("qkv", _Weight), ("out", _Weight), ("up", _Weight), ("down", _Weight)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"g.build()'` (hipcc, gfx950).  There is no fallback implementation.")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    W, B = C.POINTER(_Weight), C.POINTER(_Block)
+    sig = {
+        "qg_abi_version": (C.c_int, []),
+        "qg_layout_version": (C.c_int, []),
+        "qg_last_error": (C.c_char_p, []),
+        "qg_pack": (C.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "qg_gemm_int4": (C.c_int, [vp, i64, W, vp, i64, i32, vp, sz, vp]),
+        "qg_gemm_int2": (C.c_int, [vp, i64, W, vp, i64, i32, vp, sz, vp]),
+        "qg_gemm_ws_bytes": (sz, [W, i32]),
+        "qg_loop_range": (C.c_int, [B, vp, i32, i32, i32, vp, sz, vp]),
+        "qg_loop_scratch_bytes": (sz, [B, i32]),
+        "qg_loop_scratch_offsets": (C.c_int, [B, i32, C.POINTER(sz), C.POINTER(sz),
+                                              C.POINTER(sz), C.POINTER(sz)]),
+        "qg_unpack": (C.c_int, [W, vp, vp]),
+        "qg_dequant": (C.c_int, [W, i32, vp, vp]),
+        "qg_release_cache": (None, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int):
+    if status != QG_OK:
+        msg = lib.qg_last_error().decode()
+        cls = QGValueError if status in (QG_EINVAL, QG_EUNSUPPORTED) else QGError
+        raise cls(fn, status, msg)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def qg_abi_version() -> int:
+    return lib.qg_abi_version()
+
+
+def qg_layout_version() -> int:
+    return lib.qg_layout_version()
+
+
+def qg_last_error() -> str:
+    return lib.qg_last_error().decode()
+
+
+@dataclass
+class PackedWeight:
+    """Layout-v1 packed weight: codes int32 [N][K*bits/32] (uint32 bit
+    patterns), scales/zeros float16 [N][K/128]."""
+    bits: int
+    K: int
+    N: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor
+    group: int = GROUP
+
+    def cstruct(self) -> _Weight:
+        return _Weight(self.bits, self.K, self.N, self.group, self.codes.data_ptr(),
+                       self.scales.data_ptr(), self.zeros.data_ptr())
+
+    @staticmethod
+    def empty(K: int, N: int, bits: int, device="cuda") -> "PackedWeight":
+        return PackedWeight(bits, K, N,
+                            torch.empty((N, K * bits // 32), dtype=torch.int32, device=device),
+                            torch.empty((N, K // GROUP), dtype=torch.float16, device=device),
+                            torch.empty((N, K // GROUP), dtype=torch.float16, device=device))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
+
+
+def qg_pack(W: torch.Tensor, bits: int, group: int = GROUP, out: PackedWeight | None = None,
+            stream=None) -> PackedWeight:
+    """Quantise FP32 W [K][N] (GPU) into layout v1; synchronises the stream."""
+    if W.dtype != torch.float32 or W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a row-major FP32 [K][N] tensor")
+    K, N = W.shape
+    p = out if out is not None else PackedWeight.empty(K, N, bits, W.device)
+    _check("qg_pack", lib.qg_pack(_dev(W, "W"), W.stride(0), K, N, bits, group, p.codes.data_ptr(),
+                                  p.scales.data_ptr(), p.zeros.data_ptr(), _stream(stream)))
+    return p
+
+
+def qg_gemm_ws_bytes(w: PackedWeight, M: int) -> int:
+    ws = w.cstruct()
+    return lib.qg_gemm_ws_bytes(C.byref(ws), M)
+
+
+def _gemm(fn, name, X, w, Y, ws, stream):
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if X.dtype != torch.float16 or Y.dtype != torch.float16 or X.stride(1) != 1 or Y.stride(1) != 1:
+        raise ValueError("X and Y must be row-major FP16 tensors")
+    need = qg_gemm_ws_bytes(w, M)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_ptr, ws_bytes = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+    cw = w.cstruct()
+    _check(name, fn(_dev(X, "X"), X.stride(0), C.byref(cw), _dev(Y, "Y"), Y.stride(0), M, ws_ptr,
+                    ws_bytes, _stream(stream)))
+    return Y
+
+
+def qg_gemm_int4(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None, ws=None,
+                 stream=None) -> torch.Tensor:
+    """Y[M][N] = X[M][K] . dequant(w), FP16 in/out, FP32 accumulation."""
+    return _gemm(lib.qg_gemm_int4, "qg_gemm_int4", X, w, Y, ws, stream)
+
+
+def qg_gemm_int2(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None, ws=None,
+                 stream=None) -> torch.Tensor:
+    return _gemm(lib.qg_gemm_int2, "qg_gemm_int2", X, w, Y, ws, stream)
+
+
+@dataclass
+class Block:
+    D: int
+    F: int
+    qkv: PackedWeight
+    out: PackedWeight
+    up: PackedWeight
+    down: PackedWeight
+
+    def cstruct(self) -> _Block:
+        return _Block(self.D, self.F, self.qkv.cstruct(), self.out.cstruct(), self.up.cstruct(),
+                      self.down.cstruct())
+
+    def nbytes(self) -> int:
+        return sum(w.nbytes() for w in (self.qkv, self.out, self.up, self.down))
+
+
+def qg_loop_scratch_bytes(blk: Block, M: int) -> int:
+    b = blk.cstruct()
+    return lib.qg_loop_scratch_bytes(C.byref(b), M)
+
+
+def qg_loop_scratch_offsets(blk: Block, M: int) -> dict:
+    b = blk.cstruct()
+    vals = [C.c_size_t() for _ in range(4)]
+    _check("qg_loop_scratch_offsets",
+           lib.qg_loop_scratch_offsets(C.byref(b), M, *(C.byref(v) for v in vals)))
+    return dict(zip(("norm", "qkv", "u", "y"), (v.value for v in vals)))
+
+
+def alloc_loop_scratch(blk: Block, M: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(qg_loop_scratch_bytes(blk, M), 256), dtype=torch.uint8, device=device)
+
+
+def scratch_views(blk: Block, M: int, scratch: torch.Tensor) -> dict:
+    """FP16 views of the last iteration's intermediates inside a loop scratch."""
+    off = qg_loop_scratch_offsets(blk, M)
+    shapes = {"norm": (M, blk.D), "qkv": (M, 3 * blk.D), "u": (M, blk.F), "y": (M, blk.D)}
+    out = {}
+    for k, shp in shapes.items():
+        n = shp[0] * shp[1]
+        out[k] = scratch[off[k]:off[k] + 2 * n].view(torch.float16).view(shp)
+    return out
+
+
+def qg_loop_range(blk: Block, h: torch.Tensor, L0: int, L1: int,
+                  scratch: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Apply iterations [L0, L1) of the block in place on FP32 h [M][D]."""
+    if h.dtype != torch.float32 or not h.is_contiguous():
+        raise ValueError("h must be a contiguous FP32 [M][D] tensor")
+    M = h.shape[0]
+    if scratch is None:
+        scratch = alloc_loop_scratch(blk, M, h.device)
+    b = blk.cstruct()
+    _check("qg_loop_range", lib.qg_loop_range(C.byref(b), _dev(h, "h"), M, L0, L1,
+                                              scratch.data_ptr(),
+                                              scratch.numel() * scratch.element_size(),
+                                              _stream(stream)))
+    return h
+
+
+def qg_unpack(w: PackedWeight, stream=None) -> torch.Tensor:
+    q = torch.empty((w.N, w.K), dtype=torch.uint8, device=w.codes.device)
+    cw = w.cstruct()
+    _check("qg_unpack", lib.qg_unpack(C.byref(cw), q.data_ptr(), _stream(stream)))
+    return q
+
+
+def qg_dequant(w: PackedWeight, fp16: bool = False, stream=None) -> torch.Tensor:
+    out = torch.empty((w.N, w.K), dtype=torch.float16 if fp16 else torch.float32,
+                      device=w.codes.device)
+    cw = w.cstruct()
+    _check("qg_dequant", lib.qg_dequant(C.byref(cw), 1 if fp16 else 0, out.data_ptr(),
+                                        _stream(stream)))
+    return out
+
+
+def qg_release_cache() -> None:
+    lib.qg_release_cache()
+
+
+def pack_block(W: dict, bits: int, D: int, F: int, device="cuda") -> Block:
+    """qg_pack each of the four FP32 [K][N] projection weights of a block."""
+    ws = {}
+    for k in ("qkv", "out", "up", "down"):
+        ws[k] = qg_pack(W[k].to(device=device, dtype=torch.float32).contiguous(), bits)
+    return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"])

@@ -1,0 +1,128 @@
+// device.h -- device-side building blocks shared by every kernel of the library:
+// the packed-code extraction and dequantisation of layout v1, FP16 helpers and
+// MFMA vector types.  One definition here, so the GEMM kernels and the
+// qg_unpack / qg_dequant test exports run exactly the same code.
+//
+// Layout v1 (see include/qgemm.h): code j of a uint32 word sits at bit
+// 16*(j mod 2) + b*floor(j/2).  Codes 2i and 2i+1 therefore sit at bits b*i
+// and 16 + b*i, and one AND with (2^b - 1) * 0x00010001 followed by an OR with
+// 0x64006400 (FP16 1024.0 in both halves) yields the FP16 pair
+// (1024 + q[2i], 1024 + q[2i+1]) exactly: at 1024 the FP16 spacing is 1.0, so
+// the low mantissa bits are the code itself.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;
+constexpr uint32_t kBias2 = 0x64006400u;  // FP16 1024.0 in both halves
+
+template <int BITS>
+struct Fmt {
+    static_assert(BITS == 4 || BITS == 2, "layout v1 has 4- and 2-bit codes");
+    static constexpr int kCodesPerWord = 32 / BITS;
+    static constexpr int kPairsPerWord = kCodesPerWord / 2;
+    static constexpr int kWordsPerGroup = kGroup / kCodesPerWord;   // 16 or 8
+    static constexpr uint32_t kPairMask = ((1u << BITS) - 1u) * 0x00010001u;
+    static constexpr int kQMax = (1 << BITS) - 1;
+};
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16 as_f16(uint16_t v) { return __builtin_bit_cast(f16, v); }
+__device__ __forceinline__ uint16_t as_u16(f16 v) { return __builtin_bit_cast(uint16_t, v); }
+
+// FP16 pair (1024 + q[2i], 1024 + q[2i+1]) of codes 2i, 2i+1 of word w.
+template <int BITS>
+__device__ __forceinline__ f16x2 biased_pair(uint32_t w, int i) {
+    return as_f16x2(((w >> (BITS * i)) & Fmt<BITS>::kPairMask) | kBias2);
+}
+
+// Integer codes q[2i], q[2i+1] of word w (used by the unpack export).
+template <int BITS>
+__device__ __forceinline__ void code_pair(uint32_t w, int i, uint32_t& q0, uint32_t& q1) {
+    const uint32_t v = (w >> (BITS * i)) & Fmt<BITS>::kPairMask;
+    q0 = v & 0xFFFFu;
+    q1 = v >> 16;
+}
+
+// Per-group constants of the dequantisation w^ = (q - z) * s, as FP16 pairs:
+// nbz = -(1024 + z) (exact: z is an integer <= 15), s2 = (s, s).
+struct GroupConst {
+    f16x2 nbz;
+    f16x2 s2;
+};
+
+__device__ __forceinline__ GroupConst group_const(uint16_t s_bits, uint16_t z_bits) {
+    const f16 z = as_f16(z_bits);
+    const f16 nb = (f16)(-1024.0f) - z;
+    GroupConst c;
+    c.nbz = f16x2{nb, nb};
+    c.s2 = f16x2{as_f16(s_bits), as_f16(s_bits)};
+    return c;
+}
+
+// (q - z) as an exact FP16 pair.
+template <int BITS>
+__device__ __forceinline__ f16x2 centered_pair(uint32_t w, int i, f16x2 nbz) {
+    return biased_pair<BITS>(w, i) + nbz;
+}
+
+// fp16_rne((q - z) * s) as an FP16 pair: exact subtraction, one rounding.
+template <int BITS>
+__device__ __forceinline__ f16x2 dequant_pair_f16(uint32_t w, int i, const GroupConst& c) {
+    return centered_pair<BITS>(w, i, c.nbz) * c.s2;
+}
+
+// Exact FP32 dequant of a pair: (q - z) is exact in FP16, the product with an
+// FP16 scale is exact in FP32 (at most 4 + 11 significant bits).
+template <int BITS>
+__device__ __forceinline__ void dequant_pair_f32(uint32_t w, int i, const GroupConst& c, float& a,
+                                                 float& b) {
+    const f16x2 d = centered_pair<BITS>(w, i, c.nbz);
+    const float s = (float)c.s2.x;
+    a = (float)d.x * s;
+    b = (float)d.y * s;
+}
+
+// Nearest FP16 (ties to even) of an FP64 value, as bits; overflow -> +-inf.
+// Works on the bit pattern: the result counts quanta of 2^qe, where
+// qe = max(E, -14) - 10 for the unbiased exponent E of x, and the FP16 bit
+// pattern is ((qe + 24) << 10) + that count for normals and subnormals alike.
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    const int e = (int)((b >> 52) & 0x7ff);
+    const uint64_t m = b & 0xFFFFFFFFFFFFFull;
+    if (e == 0x7ff) return sign | (m ? 0x7e00 : 0x7c00);
+    if (e == 0) return sign;  // |x| < 2^-1022
+    const uint64_t sig = m | (1ull << 52);
+    const int E = e - 1023;
+    const int qe = (E < -14 ? -14 : E) - 10;
+    const int shift = 52 + qe - E;  // >= 42
+    if (shift > 63) return sign;
+    uint64_t r = sig >> shift;
+    const uint64_t rem = sig & ((1ull << shift) - 1ull);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (r & 1ull))) ++r;
+    const int64_t bits = ((int64_t)(qe + 24) << 10) + (int64_t)r;
+    if (bits >= 0x7c00) return sign | 0x7c00;
+    return sign | (uint16_t)bits;
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) { return (double)(float)as_f16(h); }
+
+// Round an FP32 accumulator to FP16 (round to nearest even).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((f16)v); }
+
+}  // namespace qg

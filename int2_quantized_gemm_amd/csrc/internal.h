@@ -1,0 +1,50 @@
+// internal.h -- host-side interfaces between the C-ABI layer (qgemm.hip) and the
+// kernel translation units.  Every launcher assumes its arguments were already
+// validated by the C-ABI layer and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+
+namespace qg {
+
+// ---- pack / unpack / dequant (kernels_pack.hip)
+hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, uint32_t* codes,
+                       qg_half* scales, qg_half* zeros, int* status, hipStream_t s);
+hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s);
+hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s);
+
+// ---- GEMM (kernels_gemm.hip)
+// Epilogue applied to the FP16-rounded output y16 of each element:
+//   kStore:    Y[m][n] = y16
+//   kResidual: Y[m][n] = y16 and h[m][n] += float(y16)   (h FP32 [M][ldh])
+enum Epilogue { kStore = 0, kResidual = 1 };
+
+struct GemmArgs {
+    const qg_half* X;
+    int64_t ldx;
+    const qg_weight* w;
+    qg_half* Y;
+    int64_t ldy;
+    int M;
+    Epilogue epi;
+    float* h;
+    int64_t ldh;
+    void* ws;
+    size_t ws_bytes;
+};
+
+// Which kernel family and tile a (bits, M, K, N) problem goes to.
+enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };
+GemmPath gemm_path(int bits, int M, int K, int N);
+size_t gemm_ws_bytes(int bits, int M, int K, int N);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// ---- loop glue (kernels_loop.hip)
+// norm[m][:] = fp16(LN(h[m][:])), parameter-free, eps 1e-5, FP32.
+hipError_t launch_layernorm(const float* h, int M, int D, qg_half* norm, hipStream_t s);
+
+}  // namespace qg

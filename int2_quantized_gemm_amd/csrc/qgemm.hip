@@ -1,0 +1,326 @@
+// qgemm.hip -- the C ABI of include/qgemm.h: argument validation, dispatch to
+// the kernel families, and the loop driver (run_loop_iters_range of the
+// "Warm-start mid-loop" page: iterations [L0, L1) applied in place on the
+// residual with the same weights every iteration).
+//
+// Every entry point validates all arguments on the host before enqueuing
+// anything; a failed check returns a negative status, leaves every output
+// untouched and records a message for qg_last_error() (thread-local), the way
+// the pages' errors name the failure point ("Model" page, Raises).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return QG_OK;
+}
+
+int hip_fail(const char* where, hipError_t e) {
+    return fail(QG_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Layout-v1 checks shared by every entry point taking a weight.
+int check_weight(const qg_weight* w, const char* fn, const char* name) {
+    if (!w) return fail(QG_EINVAL, "%s: %s is NULL", fn, name);
+    if (w->bits != 4 && w->bits != 2)
+        return fail(QG_EUNSUPPORTED, "%s: %s.bits = %d, layout v1 supports 4 and 2", fn, name,
+                    w->bits);
+    if (w->group != 128)
+        return fail(QG_EUNSUPPORTED, "%s: %s.group = %d, layout v1 requires 128", fn, name,
+                    w->group);
+    if (w->K <= 0 || w->K % 128 != 0)
+        return fail(QG_EINVAL, "%s: %s.K = %d must be a positive multiple of 128", fn, name, w->K);
+    if (w->N <= 0) return fail(QG_EINVAL, "%s: %s.N = %d must be positive", fn, name, w->N);
+    if (!w->codes || !w->scales || !w->zeros)
+        return fail(QG_EINVAL, "%s: %s has a NULL codes/scales/zeros pointer", fn, name);
+    if (!aligned(w->codes, 16))
+        return fail(QG_EINVAL, "%s: %s.codes must be 16-byte aligned", fn, name);
+    if (!aligned(w->scales, 2) || !aligned(w->zeros, 2))
+        return fail(QG_EINVAL, "%s: %s.scales/zeros must be 2-byte aligned", fn, name);
+    return QG_OK;
+}
+
+int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half* Y, int64_t ldy,
+               int32_t M, size_t ws_bytes, int bits, const char* fn) {
+    int st = check_weight(w, fn, "w");
+    if (st) return st;
+    if (w->bits != bits)
+        return fail(QG_EINVAL, "%s: w->bits = %d but this entry point computes %d-bit weights", fn,
+                    w->bits, bits);
+    if (M < 0) return fail(QG_EINVAL, "%s: M = %d must be >= 0", fn, M);
+    if (M == 0) return QG_OK;
+    if (!X || !Y) return fail(QG_EINVAL, "%s: X or Y is NULL", fn);
+    if (ldx < w->K || ldx % 8 != 0)
+        return fail(QG_EINVAL, "%s: ldx = %lld must be >= K = %d and a multiple of 8", fn,
+                    (long long)ldx, w->K);
+    if (ldy < w->N || ldy % 8 != 0)
+        return fail(QG_EINVAL, "%s: ldy = %lld must be >= N = %d and a multiple of 8", fn,
+                    (long long)ldy, w->N);
+    if (!aligned(X, 16) || !aligned(Y, 16))
+        return fail(QG_EINVAL, "%s: X and Y must be 16-byte aligned", fn);
+    const size_t need = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
+    if (ws_bytes < need)
+        return fail(QG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                    ws_bytes, need);
+    return QG_OK;
+}
+
+// ---- loop scratch layout: norm [M][D], qkv [M][3D], u [M][F], y [M][D] (FP16),
+// then the GEMM workspace; every region 256-byte aligned.
+struct LoopLayout {
+    size_t norm, qkv, u, y, ws, ws_bytes, total;
+};
+
+LoopLayout loop_layout(const qg_block* b, int32_t M) {
+    LoopLayout L{};
+    const size_t m = (size_t)M;
+    L.norm = 0;
+    L.qkv = align_up(L.norm + m * b->D * 2, 256);
+    L.u = align_up(L.qkv + m * 3 * b->D * 2, 256);
+    L.y = align_up(L.u + m * b->F * 2, 256);
+    L.ws = align_up(L.y + m * b->D * 2, 256);
+    size_t ws = 0;
+    const qg_weight* ws_list[4] = {&b->qkv, &b->out, &b->up, &b->down};
+    for (const qg_weight* w : ws_list) {
+        const size_t n = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
+        ws = n > ws ? n : ws;
+    }
+    L.ws_bytes = ws;
+    L.total = align_up(L.ws + ws, 256);
+    return L;
+}
+
+int check_block(const qg_block* b, const char* fn) {
+    if (!b) return fail(QG_EINVAL, "%s: blk is NULL", fn);
+    if (b->D <= 0 || b->D % 128 != 0 || b->D > 8192)
+        return fail(QG_EINVAL, "%s: D = %d must be a positive multiple of 128, at most 8192", fn,
+                    b->D);
+    if (b->F <= 0 || b->F % 128 != 0)
+        return fail(QG_EINVAL, "%s: F = %d must be a positive multiple of 128", fn, b->F);
+    struct {
+        const qg_weight* w;
+        const char* name;
+        int K, N;
+    } ws[4] = {{&b->qkv, "qkv", b->D, 3 * b->D},
+               {&b->out, "out", b->D, b->D},
+               {&b->up, "up", b->D, b->F},
+               {&b->down, "down", b->F, b->D}};
+    for (auto& e : ws) {
+        int st = check_weight(e.w, fn, e.name);
+        if (st) return st;
+        if (e.w->K != e.K || e.w->N != e.N)
+            return fail(QG_EINVAL, "%s: %s is %dx%d (KxN) but the block needs %dx%d", fn, e.name,
+                        e.w->K, e.w->N, e.K, e.N);
+    }
+    return QG_OK;
+}
+
+// Per-device status word for qg_pack (library-owned, freed by qg_release_cache).
+std::mutex g_pack_mu;
+int* g_pack_status[64] = {nullptr};
+
+}  // namespace
+
+extern "C" {
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+int qg_layout_version(void) { return QG_LAYOUT_VERSION; }
+const char* qg_last_error(void) { return g_last_error.c_str(); }
+
+int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int32_t group,
+            uint32_t* codes, qg_half* scales, qg_half* zeros, void* stream) {
+    const char* fn = "qg_pack";
+    if (bits != 4 && bits != 2)
+        return fail(QG_EUNSUPPORTED, "%s: bits = %d, layout v1 supports 4 and 2", fn, bits);
+    if (group != 128)
+        return fail(QG_EUNSUPPORTED, "%s: group = %d, layout v1 requires 128", fn, group);
+    if (K <= 0 || K % 128 != 0)
+        return fail(QG_EINVAL, "%s: K = %d must be a positive multiple of 128", fn, K);
+    if (N <= 0) return fail(QG_EINVAL, "%s: N = %d must be positive", fn, N);
+    if (ldw < N) return fail(QG_EINVAL, "%s: ldw = %lld must be >= N = %d", fn, (long long)ldw, N);
+    if (!W || !codes || !scales || !zeros)
+        return fail(QG_EINVAL, "%s: W, codes, scales and zeros must be non-NULL", fn);
+    if (!aligned(W, 4) || !aligned(codes, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+    hipStream_t s = (hipStream_t)stream;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    if (!g_pack_status[dev]) {
+        e = hipMalloc((void**)&g_pack_status[dev], sizeof(int));
+        if (e != hipSuccess) {
+            g_pack_status[dev] = nullptr;
+            return fail(QG_ENOMEM, "%s: cannot allocate the 4-byte status word (%s)", fn,
+                        hipGetErrorString(e));
+        }
+    }
+    int* st = g_pack_status[dev];
+    if ((e = hipMemsetAsync(st, 0, sizeof(int), s)) != hipSuccess) return hip_fail(fn, e);
+    if ((e = qg::launch_pack(W, ldw, K, N, bits, codes, scales, zeros, st, s)) != hipSuccess)
+        return hip_fail(fn, e);
+    int host = 0;
+    if ((e = hipMemcpyAsync(&host, st, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return hip_fail(fn, e);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(fn, e);
+    if (host)
+        return fail(QG_EINVAL, "%s: W holds a non-finite value or a group whose scale overflows "
+                               "FP16", fn);
+    return ok();
+}
+
+size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M) {
+    if (!w || (w->bits != 4 && w->bits != 2) || M < 0) return 0;
+    return qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
+}
+
+static int gemm_entry(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
+                      int32_t M, void* ws, size_t ws_bytes, void* stream, int bits,
+                      const char* fn) {
+    int st = check_gemm(X, ldx, w, Y, ldy, M, ws_bytes, bits, fn);
+    if (st) return st;
+    if (M == 0) return ok();
+    qg::GemmArgs a{X, ldx, w, Y, ldy, M, qg::kStore, nullptr, 0, ws, ws_bytes};
+    hipError_t e = qg::launch_gemm(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+int qg_gemm_int4(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
+                 int32_t M, void* ws, size_t ws_bytes, void* stream) {
+    return gemm_entry(X, ldx, w, Y, ldy, M, ws, ws_bytes, stream, 4, "qg_gemm_int4");
+}
+
+int qg_gemm_int2(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
+                 int32_t M, void* ws, size_t ws_bytes, void* stream) {
+    return gemm_entry(X, ldx, w, Y, ldy, M, ws, ws_bytes, stream, 2, "qg_gemm_int2");
+}
+
+size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M) {
+    if (!blk || M < 0 || blk->D <= 0 || blk->F <= 0) return 0;
+    return loop_layout(blk, M).total;
+}
+
+int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t* qkv, size_t* u,
+                            size_t* y) {
+    int st = check_block(blk, "qg_loop_scratch_offsets");
+    if (st) return st;
+    if (M < 0) return fail(QG_EINVAL, "qg_loop_scratch_offsets: M = %d must be >= 0", M);
+    const LoopLayout L = loop_layout(blk, M);
+    if (norm) *norm = L.norm;
+    if (qkv) *qkv = L.qkv;
+    if (u) *u = L.u;
+    if (y) *y = L.y;
+    return ok();
+}
+
+int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1, void* scratch,
+                  size_t scratch_bytes, void* stream) {
+    const char* fn = "qg_loop_range";
+    int st = check_block(blk, fn);
+    if (st) return st;
+    if (M < 0) return fail(QG_EINVAL, "%s: M = %d must be >= 0", fn, M);
+    if (L0 < 0 || L1 < L0)
+        return fail(QG_EINVAL, "%s: need 0 <= L0 <= L1, got L0 = %d, L1 = %d", fn, L0, L1);
+    if (M == 0 || L0 == L1) return ok();
+    if (!h || !aligned(h, 16)) return fail(QG_EINVAL, "%s: h must be a 16-byte aligned pointer", fn);
+    const LoopLayout L = loop_layout(blk, M);
+    if (!scratch || !aligned(scratch, 256))
+        return fail(QG_EINVAL, "%s: scratch must be a 256-byte aligned pointer", fn);
+    if (scratch_bytes < L.total)
+        return fail(QG_EINVAL, "%s: scratch of %zu bytes is smaller than the %zu required", fn,
+                    scratch_bytes, L.total);
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)scratch;
+    qg_half* norm = (qg_half*)(base + L.norm);
+    qg_half* qkv = (qg_half*)(base + L.qkv);
+    qg_half* u = (qg_half*)(base + L.u);
+    qg_half* y = (qg_half*)(base + L.y);
+    void* ws = base + L.ws;
+    const int D = blk->D, F = blk->F;
+    hipError_t e = hipSuccess;
+    for (int32_t l = L0; l < L1 && e == hipSuccess; ++l) {
+        e = qg::launch_layernorm(h, M, D, norm, s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws,
+                                 L.ws_bytes},
+                                s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({qkv + 2 * D, 3 * D, &blk->out, y, D, M, qg::kResidual, h, D, ws,
+                                 L.ws_bytes},
+                                s);
+        if (e == hipSuccess) e = qg::launch_layernorm(h, M, D, norm, s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({norm, D, &blk->up, u, F, M, qg::kStore, nullptr, 0, ws,
+                                 L.ws_bytes},
+                                s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
+                                s);
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+int qg_unpack(const qg_weight* w, uint8_t* q, void* stream) {
+    int st = check_weight(w, "qg_unpack", "w");
+    if (st) return st;
+    if (!q) return fail(QG_EINVAL, "qg_unpack: q is NULL");
+    hipError_t e = qg::launch_unpack(*w, q, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("qg_unpack", e);
+    return ok();
+}
+
+int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream) {
+    int st = check_weight(w, "qg_dequant", "w");
+    if (st) return st;
+    if (!out || !aligned(out, 4)) return fail(QG_EINVAL, "qg_dequant: out must be 4-byte aligned");
+    hipError_t e = qg::launch_dequant(*w, out_fp16 != 0, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("qg_dequant", e);
+    return ok();
+}
+
+void qg_release_cache(void) {
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    bool any = false;
+    for (int* p : g_pack_status) any |= p != nullptr;
+    if (!any) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (int d = 0; d < 64; ++d) {
+        if (g_pack_status[d]) {
+            (void)hipSetDevice(d);
+            (void)hipDeviceSynchronize();
+            (void)hipFree(g_pack_status[d]);
+            g_pack_status[d] = nullptr;
+        }
+    }
+    (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

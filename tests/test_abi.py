@@ -1,0 +1,146 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/qgemm.h declares, and rejects bad arguments on the host before
+touching the device (no kernel is launched by any call in this file)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+qg = pytest.importorskip("int2_quantized_gemm_amd")
+
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+FAKE = 1 << 20  # a 256-byte aligned, never dereferenced address
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = _declared()
+    assert "qg_pack" in names and "qg_loop_range" in names and len(names) >= 13
+    for n in names:
+        assert hasattr(qg.lib, n), f"libqgemm.so does not export {n}"
+
+
+def test_versions():
+    assert qg.qg_abi_version() == 1
+    assert qg.qg_layout_version() == 1
+    text = open(HEADER).read()
+    assert "#define QG_ABI_VERSION 1" in text and "#define QG_LAYOUT_VERSION 1" in text
+
+
+def _w(bits=4, K=2048, N=2048, group=128, codes=FAKE, scales=FAKE, zeros=FAKE):
+    return qg._Weight(bits, K, N, group, codes, scales, zeros)
+
+
+def _gemm(fn, w, X=FAKE, ldx=2048, Y=FAKE, ldy=2048, M=1, ws=None, ws_bytes=0):
+    return fn(X, ldx, C.byref(w), Y, ldy, M, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(bits=3), qg.QG_EUNSUPPORTED, "bits"),
+    (dict(group=64), qg.QG_EUNSUPPORTED, "group"),
+    (dict(K=100), qg.QG_EINVAL, "K"),
+    (dict(K=0), qg.QG_EINVAL, "K"),
+    (dict(N=0), qg.QG_EINVAL, "N"),
+    (dict(codes=0), qg.QG_EINVAL, "NULL"),
+    (dict(codes=FAKE + 4), qg.QG_EINVAL, "aligned"),
+    (dict(scales=FAKE + 1), qg.QG_EINVAL, "aligned"),
+])
+def test_gemm_rejects_bad_weight(kw, code, needle):
+    st = _gemm(qg.lib.qg_gemm_int4, _w(**kw))
+    assert st == code
+    assert needle in qg.qg_last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ldx=2040), "ldx"), (dict(ldx=2052), "ldx"), (dict(ldy=100), "ldy"),
+    (dict(M=-1), "M"), (dict(X=0), "NULL"), (dict(Y=FAKE + 2), "aligned"),
+])
+def test_gemm_rejects_bad_operands(kw, needle):
+    assert _gemm(qg.lib.qg_gemm_int4, _w(), **kw) == qg.QG_EINVAL
+    assert needle in qg.qg_last_error()
+
+
+def test_gemm_bits_must_match_entry_point():
+    assert _gemm(qg.lib.qg_gemm_int2, _w(bits=4)) == qg.QG_EINVAL
+    assert "bits" in qg.qg_last_error()
+    assert _gemm(qg.lib.qg_gemm_int4, _w(bits=2)) == qg.QG_EINVAL
+
+
+def test_gemm_m0_is_a_noop_without_device_work():
+    assert _gemm(qg.lib.qg_gemm_int4, _w(), M=0, X=None, Y=None) == qg.QG_OK
+    assert qg.qg_last_error() == ""
+    assert qg.lib.qg_gemm_ws_bytes(C.byref(_w()), 1) == 0
+
+
+def _block(D=256, F=512, bits=4, **over):
+    ws = dict(qkv=_w(bits, D, 3 * D), out=_w(bits, D, D), up=_w(bits, D, F), down=_w(bits, F, D))
+    ws.update(over)
+    return qg._Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"])
+
+
+def _loop(b, h=FAKE, M=1, L0=0, L1=1, scratch=FAKE, nbytes=1 << 30):
+    return qg.lib.qg_loop_range(C.byref(b), h, M, L0, L1, scratch, nbytes, None)
+
+
+def test_loop_validation():
+    b = _block()
+    assert _loop(b, L0=2, L1=1) == qg.QG_EINVAL and "L0" in qg.qg_last_error()
+    assert _loop(b, L0=-1, L1=1) == qg.QG_EINVAL
+    assert _loop(b, M=-2) == qg.QG_EINVAL
+    assert _loop(_block(out=_w(4, 256, 128))) == qg.QG_EINVAL and "out" in qg.qg_last_error()
+    assert _loop(_block(D=200)) == qg.QG_EINVAL
+    assert _loop(_block(up=_w(3, 256, 512))) == qg.QG_EUNSUPPORTED
+    need = qg.lib.qg_loop_scratch_bytes(C.byref(b), 4)
+    assert need > 0
+    assert _loop(b, M=4, nbytes=need - 1) == qg.QG_EINVAL and "scratch" in qg.qg_last_error()
+    assert _loop(b, scratch=FAKE + 16) == qg.QG_EINVAL
+    assert _loop(b, h=FAKE + 4) == qg.QG_EINVAL
+    # empty ranges and M == 0 are no-ops that touch nothing
+    assert _loop(b, L0=3, L1=3) == qg.QG_OK
+    assert _loop(b, M=0) == qg.QG_OK
+
+
+def test_loop_scratch_layout_is_documented_and_aligned():
+    D, F, M = 2048, 8192, 512
+    b = _block(D, F)
+    vals = [C.c_size_t() for _ in range(4)]
+    assert qg.lib.qg_loop_scratch_offsets(C.byref(b), M, *(C.byref(v) for v in vals)) == 0
+    norm, qkv, u, y = (v.value for v in vals)
+    assert norm == 0 and qkv >= M * D * 2 and u >= qkv + M * 3 * D * 2 and y >= u + M * F * 2
+    assert all(o % 256 == 0 for o in (norm, qkv, u, y))
+    assert qg.lib.qg_loop_scratch_bytes(C.byref(b), M) >= y + M * D * 2
+
+
+def test_pack_validation():
+    f = qg.lib.qg_pack
+    assert f(FAKE, 64, 128, 64, 3, 128, FAKE, FAKE, FAKE, None) == qg.QG_EUNSUPPORTED
+    assert f(FAKE, 64, 128, 64, 4, 32, FAKE, FAKE, FAKE, None) == qg.QG_EUNSUPPORTED
+    assert f(FAKE, 64, 100, 64, 4, 128, FAKE, FAKE, FAKE, None) == qg.QG_EINVAL
+    assert f(FAKE, 32, 128, 64, 4, 128, FAKE, FAKE, FAKE, None) == qg.QG_EINVAL
+    assert "ldw" in qg.qg_last_error()
+    assert f(0, 64, 128, 64, 4, 128, FAKE, FAKE, FAKE, None) == qg.QG_EINVAL
+    assert f(FAKE + 2, 64, 128, 64, 4, 128, FAKE, FAKE, FAKE, None) == qg.QG_EINVAL
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        qg.qg_pack(torch.zeros(128, 8), 4)
+
+
+def test_product_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "int2_quantized_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "liboracle" not in text, f
+                assert "from oracle" not in text, f

@@ -1,0 +1,169 @@
+"""GPU parity of qg_gemm_int4 / qg_gemm_int2 against the FP64 oracle.
+
+Both sides quantise the same seeded FP32 weights independently (their packs
+are bit-identical, see test_gpu_pack.py) and multiply the same FP16
+activations.  Tolerance: rel-L2 <= 2e-3 and max-abs <= 1e-2.  Hand-built
+integer-exact, one-hot and cancellation cases must match bit for bit.  All
+three kernel families (GEMV M == 1, skinny MFMA 2 <= M <= 16, tiled MFMA
+M > 16) are covered at ragged shapes, with canary bands around the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import Guarded, assert_close, f16_bits, to_gpu
+
+qg = pytest.importorskip("int2_quantized_gemm_amd")
+pytestmark = pytest.mark.gpu
+
+GEMM = {4: qg.qg_gemm_int4, 2: qg.qg_gemm_int2} if hasattr(qg, "qg_gemm_int4") else {}
+
+
+def _run(bits, X: torch.Tensor, p, ld_pad: int = 0):
+    M = X.shape[0]
+    g = Guarded(M, p.N, p.N + ld_pad)
+    GEMM[bits](X, p, Y=g.view)
+    torch.cuda.synchronize()
+    g.check()
+    return g.view.float().cpu().numpy()
+
+
+def _case(orc, bits, M, K, N, seed, ld_pad=0, ldx_pad=0):
+    W, X = workloads.single_gemm(M, K, N, seed=seed)
+    p = qg.qg_pack(W.cuda(), bits)
+    op = orc.pack(W.numpy(), bits)
+    Xd = torch.zeros(M, K + ldx_pad, dtype=torch.float16, device="cuda")
+    Xd[:, :K] = X.cuda()
+    Y = _run(bits, Xd[:, :K], p, ld_pad)
+    ref = orc.gemm(X.numpy(), op)
+    return Y, ref
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 16, 17, 31, 64, 129])
+@pytest.mark.parametrize("K,N", [(128, 8), (384, 40), (2048, 200), (8192, 72)])
+def test_gemm_ragged_shapes(orc, bits, M, K, N):
+    Y, ref = _case(orc, bits, M, K, N, seed=M * 131 + K + N, ld_pad=8, ldx_pad=8)
+    assert_close(Y, ref, f"bits={bits} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("K", [512, 1024, 2048, 4096, 8192, 16384])
+def test_gemv_k_variants(orc, bits, K):
+    """Every lane/chunk arrangement of the M == 1 kernel."""
+    Y, ref = _case(orc, bits, 1, K, 264, seed=K + bits)
+    assert_close(Y, ref, f"gemv bits={bits} K={K}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (1, 2048, 6144), (1, 2048, 8192),
+                                   (1, 8192, 2048), (16, 2048, 6144), (16, 8192, 2048),
+                                   (128, 2048, 8192), (512, 2048, 2048)])
+def test_gemm_block_shapes(orc, bits, M, K, N):
+    """The measured shapes (loop-block projections at the measured M)."""
+    Y, ref = _case(orc, bits, M, K, N, seed=7)
+    assert_close(Y, ref, f"bits={bits} M={M} K={K} N={N}")
+
+
+def test_gemm_c1_seed0(orc):
+    """Single INT4 GEMM, M=1, K=N=2048, seed 0 -- the single-pass workload."""
+    Y, ref = _case(orc, 4, 1, 2048, 2048, seed=0)
+    assert_close(Y, ref, "c1")
+
+
+def test_gemm_long_prefill_down_proj_sampled_rows(orc):
+    """M=2048 through the FFN down projection (K=8192 -> N=2048): the GPU runs
+    all rows in the launch configuration the bench times; the oracle checks a
+    sample of rows (rows are independent)."""
+    W, X = workloads.single_gemm(2048, 8192, 2048, seed=0)
+    p = qg.qg_pack(W.cuda(), 4)
+    op = orc.pack(W.numpy(), 4)
+    Y = qg.qg_gemm_int4(X.cuda(), p).float().cpu().numpy()
+    rows = [0, 1, 127, 128, 1000, 2047]
+    ref = orc.gemm(X.numpy()[rows], op)
+    assert_close(Y[rows], ref, "m2048 down sampled")
+    assert np.all(np.isfinite(Y))
+
+
+def _packed_from_codes(orc, bits, q, s, z):
+    q = np.asarray(q, np.int64)
+    N, K = q.shape
+    per = 32 // bits
+    words = np.zeros((N, K // per), np.uint64)
+    for j in range(per):
+        words |= q[:, j::per].astype(np.uint64) << np.uint64(16 * (j % 2) + bits * (j // 2))
+    return orc.Packed(bits, K, N, words.astype(np.uint32),
+                      orc.half_bits(np.asarray(s, np.float64).reshape(N, K // 128)),
+                      orc.half_bits(np.asarray(z, np.float64).reshape(N, K // 128)))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [1, 5, 16, 40])
+def test_gemm_integer_exact(orc, bits, M):
+    rng = np.random.default_rng(100 + M)
+    K, N = 2048, 48
+    q = rng.integers(0, 1 << bits, size=(N, K))
+    z = rng.integers(0, 1 << bits, size=(N, K // 128))
+    op = _packed_from_codes(orc, bits, q, np.full(N * K // 128, 2.0 ** -4), z)
+    X = np.zeros((M, K), np.float16)
+    for m in range(M):
+        idx = rng.choice(K, 8, replace=False)
+        X[m, idx] = rng.choice([-1, 1], 8)
+    ref = orc.gemm(X, op)
+    Y = GEMM[bits](torch.from_numpy(X).cuda(), to_gpu(op, qg))
+    assert np.array_equal(f16_bits(Y), orc.half_bits(ref))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_gemm_one_hot_rows(orc, bits, M):
+    W, _ = workloads.single_gemm(1, 2048, 136, seed=5)
+    p = qg.qg_pack(W.cuda(), bits)
+    op = orc.pack(W.numpy(), bits)
+    ks = (np.arange(M) * 97) % 2048
+    X = np.zeros((M, 2048), np.float16)
+    X[np.arange(M), ks] = 1.0
+    Y = f16_bits(GEMM[bits](torch.from_numpy(X).cuda(), p))
+    dq = orc.dequant(op)                       # [N][K]
+    assert np.array_equal(Y, orc.half_bits(dq[:, ks].T))
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_gemm_cancellation(orc, M):
+    """Partial sums reach 4096*7.5 code units while the exact result is -0.5:
+    an FP16 accumulator would lose it, FP32 accumulation keeps it exact."""
+    K, N = 8192, 16
+    half = K // 2
+    q = np.full((N, K), 15, np.int64)
+    q[:, half - 1] = 14
+    op = _packed_from_codes(orc, 4, q, np.full(N * K // 128, 0.5), np.zeros(N * K // 128))
+    X = np.ones((M, K), np.float16)
+    X[:, half:] = -1
+    Y = qg.qg_gemm_int4(torch.from_numpy(X).cuda(), to_gpu(op, qg)).float().cpu().numpy()
+    assert np.all(Y == -0.5)
+    assert np.all(orc.gemm(X[:1], op) == -0.5)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [1, 16, 512])
+def test_gemm_deterministic(bits, M):
+    W, X = workloads.single_gemm(M, 2048, 2048, seed=3)
+    p = qg.qg_pack(W.cuda(), bits)
+    Xd = X.cuda()
+    Ys = [f16_bits(GEMM[bits](Xd, p)) for _ in range(3)]
+    assert np.array_equal(Ys[0], Ys[1]) and np.array_equal(Ys[0], Ys[2])
+
+
+def test_gemm_m0_is_noop():
+    W, _ = workloads.single_gemm(1, 256, 64, seed=1)
+    p = qg.qg_pack(W.cuda(), 4)
+    Y = qg.qg_gemm_int4(torch.zeros(0, 256, dtype=torch.float16, device="cuda"), p)
+    assert Y.shape == (0, 64)
+
+
+def test_gemm_rejects_mismatched_bits():
+    W, X = workloads.single_gemm(1, 256, 64, seed=1)
+    p = qg.qg_pack(W.cuda(), 4)
+    with pytest.raises(qg.QGValueError):
+        qg.qg_gemm_int2(X.cuda(), p)

@@ -1,0 +1,93 @@
+"""GPU parity of qg_pack, qg_unpack and qg_dequant against the oracle: bit-exact
+codes, scales and zeros; bit-exact unpacked codes; FP32 dequant equal to the
+oracle's exact value and FP16 dequant equal to its round-to-nearest-even."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import f16_bits, to_gpu
+
+qg = pytest.importorskip("int2_quantized_gemm_amd")
+pytestmark = pytest.mark.gpu
+
+
+def _pack_both(orc, W: np.ndarray, bits: int):
+    p = qg.qg_pack(torch.from_numpy(W).cuda(), bits)
+    op = orc.pack(W, bits)
+    return p, op
+
+
+def _assert_pack_equal(p, op):
+    assert np.array_equal(p.codes.cpu().numpy().view(np.uint32), op.codes)
+    assert np.array_equal(f16_bits(p.scales), op.scales)
+    assert np.array_equal(f16_bits(p.zeros), op.zeros)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("K,N", [(128, 1), (256, 37), (384, 300), (2048, 2048), (8192, 64)])
+def test_pack_bit_exact(orc, bits, K, N):
+    W, _ = workloads.single_gemm(1, K, N, seed=K + N)
+    _assert_pack_equal(*_pack_both(orc, W.numpy(), bits))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_pack_full_block_bit_exact(orc, bits):
+    """The loop block's four weights at D=2048, F=8192 (the measured shapes)."""
+    inp = workloads.block(1, seed=0)
+    for name, W in inp.W.items():
+        _assert_pack_equal(*_pack_both(orc, W.numpy(), bits))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_pack_special_groups(orc, bits):
+    rng = np.random.default_rng(3)
+    W = (rng.standard_normal((512, 40)) * 0.02).astype(np.float32)
+    W[:128, 0] = 0.0                                   # all-zero group
+    W[128:256, 1] = np.abs(W[128:256, 1])              # all positive
+    W[256:384, 2] = -np.abs(W[256:384, 2])             # all negative
+    W[5, :] = 0.0                                      # exact zeros
+    W[:128, 3] = 1e-9                                  # scale rounds to 0 -> 1
+    W[:128, 4] = 65504.0 * ((1 << bits) - 1)           # largest finite scale
+    W[:, 5] = np.where(np.arange(512) % 2 == 0, 1.0, -1.0)  # alternating +-1
+    W[:, 6] = np.ldexp(1.0, -20)                       # subnormal-range scale
+    _assert_pack_equal(*_pack_both(orc, W, bits))
+
+
+def test_pack_ldw_larger_than_n(orc):
+    W, _ = workloads.single_gemm(1, 256, 72, seed=9)
+    Wd = torch.zeros(256, 80, dtype=torch.float32)
+    Wd[:, :72] = W
+    p = qg.qg_pack(Wd.cuda()[:, :72], 4)
+    _assert_pack_equal(p, orc.pack(W.numpy(), 4))
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, 3e38])
+def test_pack_rejects_non_finite_and_overflow(bad):
+    W = np.zeros((128, 8), np.float32)
+    W[7, 3] = bad
+    with pytest.raises(qg.QGValueError):
+        qg.qg_pack(torch.from_numpy(W).cuda(), 4)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_unpack_and_dequant_bit_exact(orc, bits):
+    W, _ = workloads.single_gemm(1, 1024, 96, seed=bits)
+    p, op = _pack_both(orc, W.numpy(), bits)
+    assert np.array_equal(qg.qg_unpack(p).cpu().numpy(), orc.unpack(op))
+    ref = orc.dequant(op)
+    d32 = qg.qg_dequant(p, fp16=False).cpu().numpy().astype(np.float64)
+    assert np.array_equal(d32, ref)
+    d16 = f16_bits(qg.qg_dequant(p, fp16=True))
+    assert np.array_equal(d16, orc.half_bits(ref))
+
+
+def test_unpack_hand_built_words(orc):
+    from conftest import golden
+    for case in golden("bit_order.json")["cases"]:
+        bits, per = case["bits"], 32 // case["bits"]
+        codes = np.full((1, 128 // per), int(case["word"], 16), dtype=np.uint32)
+        op = orc.Packed(bits, 128, 1, codes, np.full((1, 1), 0x3C00, np.uint16),
+                        np.zeros((1, 1), np.uint16))
+        q = qg.qg_unpack(to_gpu(op, qg)).cpu().numpy()[0]
+        assert list(q[:per]) == case["codes"]
