@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only INT4/INT2 quantised GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input: the
+INT4 loop block (D=2048: QKV 2048->6144, out 2048->2048, FFN up 2048->8192,
+down 8192->2048, group 128) applied for L=8 iterations at M=1 decode through
+qg_loop_range -- every GEMM of those iterations, the LayerNorm glue and the
+residual epilogues.  Weights are packed once beforehand (they arrive packed at
+model load).  The residual h lives in one buffer, like the runtime's FP32
+residual stream: each step applies the block's L iterations to the state the
+previous step left (the same work whatever the values), so nothing but the
+hot path runs inside the timed region.  `value` is the effective weight
+bandwidth: steps * L * (packed block bytes: codes + scales + zeros) / wall
+time.
+
+The JSON line also carries
+  * roofline: the dominant kernel of the step (the FFN down-projection GEMV,
+    K=8192, N=2048, the same kernel and grid as inside the loop) timed with
+    HIP events on the stream it runs on, over a captured batch of
+    back-to-back launches on the same, cache-warm weights, against the
+    8 TB/s HBM peak;
+  * cpu_baseline: the FP64 CPU oracle timed on the host cores on a bounded
+    sample of the same workload (whole L=8 steps for ~10 s);
+  * extra: the other measured workloads (single-pass INT4 GEMM over a 535 MB
+    rotation pool, cold single-pass block, M=512 prefill TFLOP/s, the INT2
+    block, M=16 decode for L=32 and the M=2048 down projection).
+Diagnostics go to stderr; stdout holds the one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA
+D, F, L_MAIN = 2048, 8192, 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def block_flops(M: int, D: int = D, F: int = F) -> float:
+    return 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
+
+
+def time_loop(qg, torch, blk, h, L, scratch, steps, warmup):
+    """`warmup` untimed then `steps` timed calls of qg_loop_range(0, L) on the
+    residual h; returns the wall time of the timed calls in seconds."""
+    for _ in range(warmup):
+        qg.qg_loop_range(blk, h, 0, L, scratch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        qg.qg_loop_range(blk, h, 0, L, scratch)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def graph_leg(torch, launch, count, replays=10):
+    """Average duration (s) of one launch among `count` back-to-back launches
+    captured in a graph, timed with HIP events around the replays on the
+    stream that runs them."""
+    launch(0)  # host-side validation and warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / (replays * count)
+
+
+def traffic_record(kernel_key: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "int2_quantized_gemm_amd", "csrc", "kernels_gemm.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    e = rec.get(kernel_key)
+    if not e or e.get("source_sha256_16") != h:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float):
+    import numpy as np
+
+    import oracle
+    import workloads
+    inp = workloads.block(1, seed=0)
+    ob = oracle.pack_block({k: v.numpy() for k, v in inp.W.items()}, 4, D, F)
+    h0 = inp.X.numpy().astype(np.float64)
+    block_bytes = sum(p.codes.nbytes + p.scales.nbytes + p.zeros.nbytes
+                      for p in (ob.qkv, ob.out, ob.up, ob.down))
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.loop_range(ob, h0, 0, L_MAIN)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": round(steps * L_MAIN * block_bytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{steps} whole steps of the same workload (INT4 block, M=1, L={L_MAIN}, "
+                  f"seed 0) through the FP64 oracle, {el:.1f} s wall",
+        "seconds": round(el, 2),
+    }
+
+
+def extra_legs(qg, torch, workloads, args):
+    out = {}
+    dev = "cuda"
+
+    def sync():
+        torch.cuda.synchronize()
+
+    # c1: single INT4 GEMM M=1 K=N=2048 over a >= 512 MB rotation pool (HBM,
+    # single pass: no copy is re-read before the pool wraps).
+    W, X = workloads.single_gemm(1, 2048, 2048, seed=0)
+    p = qg.qg_pack(W.to(dev), 4)
+    pool = [qg.PackedWeight(4, 2048, 2048, p.codes.clone(), p.scales.clone(), p.zeros.clone())
+            for _ in range(240)]
+    Xd, Y = X.to(dev), torch.empty(1, 2048, dtype=torch.float16, device=dev)
+    per = graph_leg(torch, lambda i: qg.qg_gemm_int4(Xd, pool[i], Y=Y), len(pool), replays=4)
+    out["c1_int4_gemm_m1_pool"] = {
+        "us_per_call": round(per * 1e6, 3), "GB/s": round(p.nbytes() / per / 1e9, 1),
+        "frac_hbm": round(p.nbytes() / per / 1e9 / HBM_PEAK_GBS, 4),
+        "pool_MB": round(len(pool) * p.nbytes() / 1e6, 1)}
+    del pool
+    sync()
+
+    def loop_case(name, bits, M, L):
+        inp = workloads.block(M, seed=0)
+        blk = qg.pack_block(inp.W, bits, D, F)
+        scratch = qg.alloc_loop_scratch(blk, M)
+        h = inp.X.float().to(dev)
+        t1 = time_loop(qg, torch, blk, h, L, scratch, 1, 2)
+        reps = int(max(3, min(200, 0.3 / max(t1, 1e-6))))
+        per = time_loop(qg, torch, blk, h, L, scratch, reps, 1) / reps
+        r = {"M": M, "L": L, "bits": bits, "ms_per_call": round(per * 1e3, 4),
+             "eff_weight_GB/s": round(L * blk.nbytes() / per / 1e9, 1),
+             "TFLOP/s": round(block_flops(M) * L / per / 1e12, 2)}
+        r["frac_hbm"] = round(r["eff_weight_GB/s"] / HBM_PEAK_GBS, 4)
+        r["frac_mfma"] = round(r["TFLOP/s"] / MFMA_F16_PEAK_TFLOPS, 4)
+        out[name] = r
+
+    # c2 cold: L=1 over a rotation pool of 20 distinct blocks (535 MB).
+    inp = workloads.block(1, seed=0)
+    blk = qg.pack_block(inp.W, 4, D, F)
+    copies = []
+    for _ in range(20):
+        copies.append(qg.Block(D, F, *(qg.PackedWeight(w.bits, w.K, w.N, w.codes.clone(),
+                                                      w.scales.clone(), w.zeros.clone())
+                                       for w in (blk.qkv, blk.out, blk.up, blk.down))))
+    scratch = qg.alloc_loop_scratch(blk, 1)
+    h = inp.X.float().to(dev)
+    for b in copies:
+        qg.qg_loop_range(b, h, 0, 1, scratch)
+    sync()
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for b in copies:
+            qg.qg_loop_range(b, h, 0, 1, scratch)
+    sync()
+    cold = (time.perf_counter() - t0) / (reps * len(copies))
+    out["c2_int4_block_m1_cold_l1"] = {"ms_per_iteration": round(cold * 1e3, 4),
+                                       "GB/s": round(blk.nbytes() / cold / 1e9, 1)}
+    del copies
+    sync()
+
+    loop_case("c3_int4_block_m512_l8", 4, 512, 8)
+    loop_case("c4a_int2_block_m1_l16", 2, 1, 16)
+    loop_case("c4b_int2_block_m128_l8", 2, 128, 8)
+    loop_case("c5a_int4_block_m16_l32", 4, 16, 32)
+
+    # c5b: M=2048 single-shot prefill through the down projection K=8192 -> N=2048.
+    W, X = workloads.single_gemm(2048, 8192, 2048, seed=0)
+    p = qg.qg_pack(W.to(dev), 4)
+    Xd, Y = X.to(dev), torch.empty(2048, 2048, dtype=torch.float16, device=dev)
+    med = graph_leg(torch, lambda i: qg.qg_gemm_int4(Xd, p, Y=Y), 10, replays=3)
+    out["c5b_int4_down_m2048"] = {"us_per_call": round(med * 1e6, 2),
+                                  "TFLOP/s": round(2.0 * 2048 * 8192 * 2048 / med / 1e12, 2),
+                                  "frac_mfma": round(2.0 * 2048 * 8192 * 2048 / med / 1e12
+                                                     / MFMA_F16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int2_quantized_gemm_amd as qg
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    # ---- main leg: INT4 loop block, M=1, L=8 (decode)
+    inp = workloads.block(1, seed=0)
+    blk = qg.pack_block(inp.W, 4, D, F, dev)
+    scratch = qg.alloc_loop_scratch(blk, 1, dev)
+    h = inp.X.float().to(dev)
+    el = time_loop(qg, torch, blk, h, L_MAIN, scratch, args.steps, args.warmup)
+    assert bool(torch.isfinite(h).all()), "residual became non-finite"
+    block_bytes = blk.nbytes()
+    value = args.steps * L_MAIN * block_bytes / el / 1e9
+    log(f"main: {args.steps} steps in {el * 1e3:.2f} ms -> {value:.1f} GB/s effective")
+
+    # ---- roofline: the dominant kernel of the step in its loop configuration
+    # (down projection: u [1][F] FP16 -> [1][D], the GEMV kernel the loop runs)
+    u = torch.empty(1, F, dtype=torch.float16, device=dev).normal_()
+    y = torch.empty(1, D, dtype=torch.float16, device=dev)
+    avg_s = graph_leg(torch, lambda i: qg.qg_gemm_int4(u, blk.down, Y=y), 200, replays=5)
+    down_bytes = blk.down.nbytes()
+    achieved = down_bytes / avg_s / 1e9
+    traffic = traffic_record("gemv_int4_k8192_n2048")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "k_gemv<4,64,4,2,false> (FFN down projection, K=8192, N=2048, M=1)",
+                "algorithmic_bytes_per_launch": down_bytes,
+                "avg_launch_us": round(avg_s * 1e6, 3)}
+    log(f"roofline: {roofline}")
+
+    result = {
+        "metric": "quant_gemm effective weight GB/s (M=1) and TFLOP/s (M=512), % of roofline",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "INT4 loop block D=2048 (QKV 2048->6144, out 2048->2048, "
+                               "up 2048->8192, down 8192->2048), group 128, M=1 decode, L=8, "
+                               "W~N(0,0.02), X~N(0,1) FP16, seed 0",
+                   "weights": "int4 asymmetric, FP16 scales/zeros",
+                   "accumulate": "f32",
+                   "block_bytes": block_bytes,
+                   "iterations_per_step": L_MAIN},
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        log(f"cpu_baseline: {result['cpu_baseline']}")
+    if not args.no_extra:
+        result["extra"] = extra_legs(qg, torch, workloads, args)
+        log(f"extra: {json.dumps(result['extra'])}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

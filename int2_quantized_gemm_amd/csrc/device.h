@@ -126,3 +126,46 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) { return (double)(
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((f16)v); }
 
 }  // namespace qg
+
+namespace qg {
+
+// ---- cross-lane sums without LDS traffic: DPP within rows of 16 lanes, then
+// v_readlane across the four rows of a wave64.  The order of additions is
+// fixed, so every lane of a segment gets bit-identical sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over each row of 16 lanes (quad_perm xor 1, xor 2, then row rotations
+// by 4 and 8), present in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    return v;
+}
+
+// Sum over aligned segments of S lanes (S = 16, 32 or 64), in every lane.
+template <int S>
+__device__ __forceinline__ float segment_sum(float v) {
+    static_assert(S == 16 || S == 32 || S == 64, "segments of 16, 32 or 64 lanes");
+    v = row16_sum(v);
+    if constexpr (S == 16) {
+        return v;
+    } else if constexpr (S == 32) {
+        const float lo = readlane_f(v, 0) + readlane_f(v, 16);
+        const float hi = readlane_f(v, 32) + readlane_f(v, 48);
+        return (threadIdx.x & 63) < 32 ? lo : hi;
+    } else {
+        return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+    }
+}
+
+}  // namespace qg

@@ -35,7 +35,15 @@ struct GemmArgs {
     int64_t ldh;
     void* ws;
     size_t ws_bytes;
+    // M == 1 GEMV only: when ln_h is set, the activations are fp16(LN(ln_h))
+    // (ln_h FP32 [K]) and X is ignored; norm_out, if set, receives them.
+    const float* ln_h = nullptr;
+    qg_half* norm_out = nullptr;
 };
+
+// True when a GEMM of this shape can take its activations as the fused
+// LayerNorm of an FP32 row (the M == 1 GEMV path).
+bool gemm_fuses_layernorm(int bits, int M, int K, int N);
 
 // Which kernel family and tile a (bits, M, K, N) problem goes to.
 enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };

@@ -5,10 +5,12 @@
 // Three kernel families, chosen by M:
 //   * k_gemv (M == 1): bandwidth-bound GEMV.  Lanes split K: each lane loads
 //     16 contiguous bytes of packed codes per chunk (a wave reads a contiguous
-//     1 KiB run of a row), converts codes with the exponent-bias trick, forms
-//     exact (q - z) FP16 pairs and accumulates x*(q - z) with v_dot2_f32_f16;
-//     the per-group scale multiplies the lane's partial once.  Lane partials of
-//     a row are combined by a fixed xor-butterfly (deterministic).
+//     1 KiB run of a row), converts codes with the exponent-bias trick and
+//     accumulates x . (1024 + 2^j q) with v_dot2_f32_f16; bias, zero point and
+//     the per-group scale are applied once per lane chunk.  Lane partials of a
+//     row are combined by a fixed xor-butterfly (deterministic).  Optionally
+//     the activations are the LayerNorm of the FP32 residual, computed in the
+//     prologue (the loop block's QKV and up projections).
 //   * k_gemm_skinny (2 <= M <= 16): one 16-row MFMA tile of output channels per
 //     workgroup, K split over the workgroup's waves and reduced through LDS in
 //     wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A (M padded to 16)
@@ -30,44 +32,98 @@ namespace {
 
 // ------------------------------------------------------------------ GEMV ----
 
+// Dot products of one lane chunk (4 packed words) with its activations.
+// Codes 2i and 2i+1 of a word sit at bits b*i and 16 + b*i.  Rather than
+// shifting every pair down, a word and its copy shifted right by 8 are each
+// masked at the NC = 8/b code positions of a byte: mask class j keeps the
+// codes at bits b*j and 16 + b*j, and OR-ing 0x6400 into both halves gives
+// the FP16 pair 1024 + 2^(b*j) * q exactly (all values stay below 2048, where
+// the FP16 spacing is 1).  Class j accumulates x . (1024 + 2^(b*j) q) in FP32
+// with v_dot2_f32_f16; the bias 1024 * sum(x) and the factor 2^(b*j) come
+// out once per chunk from precomputed activation sums.
+template <int BITS>
+struct GemvMath {
+    using F = Fmt<BITS>;
+    static constexpr int NC = 8 / BITS;   // mask classes
+    static constexpr int PPW = 16 / BITS;  // FP16 pairs per word (= 2 * NC)
+
+    // Pair index (relative to the chunk) of class j, half h (h = 1: word >> 8).
+    static __device__ __forceinline__ int pair(int q, int h, int j) { return q * PPW + j + NC * h; }
+
+    static __device__ __forceinline__ void accumulate(const u32x4& w4, const f16x2* xp,
+                                                      float acc[NC]) {
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t v[2] = {w[q], w[q] >> 8};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < NC; ++j)
+                    acc[j] = __builtin_amdgcn_fdot2(
+                        as_f16x2((v[h] & (F::kPairMask << (BITS * j))) | kBias2),
+                        xp[pair(q, h, j)], acc[j], false);
+        }
+    }
+
+    // Per-class sums of the activations of a chunk.
+    static __device__ __forceinline__ void xsums(const f16x2* xp, float xs[NC]) {
+        const f16x2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+        for (int j = 0; j < NC; ++j) xs[j] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < NC; ++j)
+                    xs[j] = __builtin_amdgcn_fdot2(xp[pair(q, h, j)], one, xs[j], false);
+    }
+
+    // sum_k x_k * (q_k - z) of the chunk, from the class accumulators.
+    static __device__ __forceinline__ float centred(const float acc[NC], const float xs[NC],
+                                                    float xs_all, float z) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            t += (acc[j] - 1024.0f * xs[j]) * (1.0f / (float)(1 << (BITS * j)));
+        return t - z * xs_all;
+    }
+};
+
 // LPR lanes cover one row per chunk of 4*LPR words; CPR chunks per row;
-// 64/LPR rows per wave step; U row steps per wave.
-template <int BITS, int LPR, int CPR, int U>
+// 64/LPR rows per wave step; U row steps per wave; K = 4*LPR*CPR*(32/b) is a
+// compile-time constant of each variant.  With LN, the activations are
+// fp16(LayerNorm(hln)): the workgroup's 256 threads normalise the row once
+// (mean, then population variance of the centred values, eps 1e-5, reduced
+// by DPP in each wave and then in wave order through LDS), stage it in LDS
+// for the lanes to pick up, and workgroup 0 also writes it to norm_out.
+template <int BITS, int LPR, int CPR, int U, bool LN>
 __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
+                                              const float* __restrict__ hln,
+                                              uint16_t* __restrict__ norm_out,
                                               const uint32_t* __restrict__ codes,
                                               const uint16_t* __restrict__ scales,
-                                              const uint16_t* __restrict__ zeros, int K, int N,
+                                              const uint16_t* __restrict__ zeros, int N,
                                               uint16_t* __restrict__ Y, float* __restrict__ h,
                                               int epi) {
     using F = Fmt<BITS>;
+    using G = GemvMath<BITS>;
     constexpr int RPW = 64 / LPR;
-    constexpr int PAIRS = 4 * F::kPairsPerWord;  // FP16 pairs of X per lane and chunk
+    constexpr int PAIRS = 4 * F::kPairsPerWord;  // FP16 pairs of x per lane and chunk
+    constexpr int K = 4 * LPR * CPR * F::kCodesPerWord;
+    constexpr int wpr = K / F::kCodesPerWord;
+    constexpr int groups = K / kGroup;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
-    const int wpr = K / F::kCodesPerWord;
-    const int groups = K / kGroup;
     const int row0 = wave * U * RPW;
-    if (row0 >= N) return;
+    const bool active = row0 < N;
+    if (!LN && !active) return;  // (LN variants keep every wave for the barriers)
 
-    // Activations for this lane's k positions, reused for every row.
-    f16x2 xr[CPR][PAIRS];
-#pragma unroll
-    for (int c = 0; c < CPR; ++c) {
-        const int k0 = (c * LPR * 4 + sub * 4) * F::kCodesPerWord;
-        const u32x4* xp = (const u32x4*)(X + k0);
-#pragma unroll
-        for (int v = 0; v < PAIRS / 4; ++v) {
-            const u32x4 t = xp[v];
-            xr[c][4 * v + 0] = as_f16x2(t.x);
-            xr[c][4 * v + 1] = as_f16x2(t.y);
-            xr[c][4 * v + 2] = as_f16x2(t.z);
-            xr[c][4 * v + 3] = as_f16x2(t.w);
-        }
-    }
-
-    // Issue every load of this wave before any arithmetic.
+    // Issue the weight loads of this wave first; the activations and their
+    // LayerNorm are computed while they are in flight.
     u32x4 wv[U][CPR];
     uint16_t sv[U][CPR], zv[U][CPR];
 #pragma unroll
@@ -89,33 +145,100 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         }
     }
 
-    float part[U];
+    // Activations for this lane's k positions, reused for every row.
+    f16x2 xr[CPR][PAIRS];
+    if constexpr (LN) {
+        constexpr int VPT = K / 256;  // values per thread
+        static_assert(VPT % 4 == 0, "K must be a multiple of 1024 for the fused LayerNorm");
+        __shared__ uint32_t xl[K / 2];
+        __shared__ float part[2][4];
+        const int t = threadIdx.x;
+        const int w = t >> 6;
+        float v[VPT];
+        const float4* hp = (const float4*)(hln + t * VPT);
+#pragma unroll
+        for (int i = 0; i < VPT / 4; ++i) {
+            const float4 q = hp[i];
+            v[4 * i] = q.x;
+            v[4 * i + 1] = q.y;
+            v[4 * i + 2] = q.z;
+            v[4 * i + 3] = q.w;
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) sum += v[i];
+        sum = segment_sum<64>(sum);
+        if (lane == 0) part[0][w] = sum;
+        __syncthreads();
+        const float mean = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) / (float)K;
+        float sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            v[i] -= mean;
+            sq += v[i] * v[i];
+        }
+        sq = segment_sum<64>(sq);
+        if (lane == 0) part[1][w] = sq;
+        __syncthreads();
+        const float var = ((part[1][0] + part[1][1]) + (part[1][2] + part[1][3])) / (float)K;
+        const float rstd = 1.0f / sqrtf(var + 1e-5f);
+#pragma unroll
+        for (int i = 0; i < VPT / 2; ++i)
+            xl[t * (VPT / 2) + i] =
+                as_u32(f16x2{(f16)(v[2 * i] * rstd), (f16)(v[2 * i + 1] * rstd)});
+        if (norm_out != nullptr && blockIdx.x == 0) {
+            uint32_t* op = (uint32_t*)norm_out + t * (VPT / 2);
+#pragma unroll
+            for (int i = 0; i < VPT / 2; ++i) op[i] = xl[t * (VPT / 2) + i];
+        }
+        __syncthreads();
+        if (!active) return;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const int p0 = (c * LPR * 4 + sub * 4) * F::kCodesPerWord / 2;
+#pragma unroll
+            for (int i = 0; i < PAIRS; ++i) xr[c][i] = as_f16x2(xl[p0 + i]);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const int k0 = (c * LPR * 4 + sub * 4) * F::kCodesPerWord;
+            const u32x4* xp = (const u32x4*)(X + k0);
+#pragma unroll
+            for (int v = 0; v < PAIRS / 4; ++v) {
+                const u32x4 t = xp[v];
+                xr[c][4 * v + 0] = as_f16x2(t.x);
+                xr[c][4 * v + 1] = as_f16x2(t.y);
+                xr[c][4 * v + 2] = as_f16x2(t.z);
+                xr[c][4 * v + 3] = as_f16x2(t.w);
+            }
+        }
+    }
+    float xs[CPR][G::NC], xs_all[CPR];
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+        G::xsums(xr[c], xs[c]);
+        xs_all[c] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < G::NC; ++j) xs_all[c] += xs[c][j];
+    }
+
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
-            const GroupConst gc = group_const(sv[u][c], zv[u][c]);
-            float a = 0.0f;
-            const uint32_t w4[4] = {wv[u][c].x, wv[u][c].y, wv[u][c].z, wv[u][c].w};
+            float a[G::NC];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int p = 0; p < F::kPairsPerWord; ++p)
-                    a = __builtin_amdgcn_fdot2(centered_pair<BITS>(w4[q], p, gc.nbz),
-                                               xr[c][q * F::kPairsPerWord + p], a, false);
-            acc += a * (float)gc.s2.x;
+            for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
+            G::accumulate(wv[u][c], xr[c], a);
+            const float t = G::centred(a, xs[c], xs_all[c], (float)as_f16(zv[u][c]));
+            acc += t * (float)as_f16(sv[u][c]);
         }
-        part[u] = acc;
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) part[u] += __shfl_xor(part[u], off);
+        acc = segment_sum<LPR>(acc);
         const int row = row0 + u * RPW + rsub;
         if (sub == 0 && row < N) {
-            const uint16_t y = f32_to_f16_bits(part[u]);
+            const uint16_t y = f32_to_f16_bits(acc);
             Y[row] = y;
             if (epi == kResidual) h[row] += (float)as_f16(y);
         }
@@ -342,42 +465,67 @@ GemvShape gemv_shape(int bits, int K) {
     return s;
 }
 
-template <int BITS, int LPR, int CPR>
-hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
+// Rows per wave U: several rows per wave amortise the activations held in
+// registers (and the fused LayerNorm) but cut the number of waves in flight.
+// Measured on MI355X with the loop block's weights cache-resident: U = 4 from
+// 8192 row steps (FFN up), U = 2 from 2048 (QKV, out, down), else U = 1; at
+// most 8 outstanding 16-byte code loads per lane (U * CPR <= 8).
+template <int BITS, int LPR, int CPR, int U, bool LN>
+hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     constexpr int RPW = 64 / LPR;
+    constexpr int kWavesPerBlock = 4;
     const int N = a.w->N;
     const int steps = (N + RPW - 1) / RPW;
-    // Several rows per wave reuse the activations held in registers; keep at
-    // least ~4 waves per CU for latency hiding.
-    int U = 1;
-    if (CPR <= 2 && steps >= 4 * 1024) U = 4;
-    else if (CPR <= 4 && steps >= 2 * 1024) U = 2;
-    const int waves_per_block = 4;
-#define QG_GEMV_LAUNCH(UU)                                                                     \
-    {                                                                                          \
-        const int waves = (steps + UU - 1) / UU;                                               \
-        const int blocks = (waves + waves_per_block - 1) / waves_per_block;                    \
-        k_gemv<BITS, LPR, CPR, UU><<<blocks, 64 * waves_per_block, 0, s>>>(                    \
-            a.X, a.w->codes, a.w->scales, a.w->zeros, a.w->K, N, a.Y, a.h, (int)a.epi);        \
-    }
-    if (U == 4) QG_GEMV_LAUNCH(4) else if (U == 2) QG_GEMV_LAUNCH(2) else QG_GEMV_LAUNCH(1)
-#undef QG_GEMV_LAUNCH
+    const int waves = (steps + U - 1) / U;
+    const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    k_gemv<BITS, LPR, CPR, U, LN><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
+        a.X, a.ln_h, a.norm_out, a.w->codes, a.w->scales, a.w->zeros, N, a.Y, a.h, (int)a.epi);
     return hipGetLastError();
+}
+
+// The fused LayerNorm needs K = 4*LPR*CPR*(32/b) to be a multiple of 1024 and
+// at most 8192 (the LN input is a residual row of D <= 8192 values).
+template <int BITS, int LPR, int CPR>
+constexpr bool ln_variant_ok() {
+    constexpr int K = 4 * LPR * CPR * (32 / BITS);
+    return K % 1024 == 0 && K <= 8192;
+}
+
+template <int BITS, int LPR, int CPR, bool LN>
+hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
+    if constexpr (LN && !ln_variant_ok<BITS, LPR, CPR>()) {
+        return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_layernorm
+    } else {
+    constexpr int RPW = 64 / LPR;
+    const int steps = (a.w->N + RPW - 1) / RPW;
+    if constexpr (CPR <= 2) {
+        if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN>(a, s);
+    }
+    if constexpr (CPR <= 4) {
+        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN>(a, s);
+    }
+    return launch_gemv_u<BITS, LPR, CPR, 1, LN>(a, s);
+    }
+}
+
+template <int BITS, bool LN>
+hipError_t launch_gemv_ln(const GemmArgs& a, hipStream_t s) {
+    const GemvShape g = gemv_shape(BITS, a.w->K);
+    if (g.lpr == 64) {
+        switch (g.cpr) {
+            case 1: return launch_gemv_t<BITS, 64, 1, LN>(a, s);
+            case 2: return launch_gemv_t<BITS, 64, 2, LN>(a, s);
+            case 4: return launch_gemv_t<BITS, 64, 4, LN>(a, s);
+            default: return launch_gemv_t<BITS, 64, 8, LN>(a, s);
+        }
+    }
+    if (g.lpr == 32) return launch_gemv_t<BITS, 32, 1, LN>(a, s);
+    return launch_gemv_t<BITS, 16, 1, LN>(a, s);
 }
 
 template <int BITS>
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
-    const GemvShape g = gemv_shape(BITS, a.w->K);
-    if (g.lpr == 64) {
-        switch (g.cpr) {
-            case 1: return launch_gemv_t<BITS, 64, 1>(a, s);
-            case 2: return launch_gemv_t<BITS, 64, 2>(a, s);
-            case 4: return launch_gemv_t<BITS, 64, 4>(a, s);
-            default: return launch_gemv_t<BITS, 64, 8>(a, s);
-        }
-    }
-    if (g.lpr == 32) return launch_gemv_t<BITS, 32, 1>(a, s);
-    return launch_gemv_t<BITS, 16, 1>(a, s);
+    return a.ln_h ? launch_gemv_ln<BITS, true>(a, s) : launch_gemv_ln<BITS, false>(a, s);
 }
 
 template <int BITS>
@@ -406,6 +554,10 @@ GemmPath gemm_path(int bits, int M, int K, int N) {
     if (M == 1 && gemv_shape(bits, K).ok) return kPathGemv;
     if (M <= 16) return kPathSkinny;
     return kPathTiled;
+}
+
+bool gemm_fuses_layernorm(int bits, int M, int K, int N) {
+    return gemm_path(bits, M, K, N) == kPathGemv && K % 1024 == 0 && K <= 8192;
 }
 
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {

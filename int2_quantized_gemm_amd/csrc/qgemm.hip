@@ -10,6 +10,9 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdlib.h>
+#include <string.h>
+#include <vector>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string>
@@ -139,6 +142,129 @@ int check_block(const qg_block* b, const char* fn) {
     return QG_OK;
 }
 
+// Enqueue `iters` iterations of the loop block on stream s (no validation).
+hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
+                        const LoopLayout& L, hipStream_t s) {
+    char* base = (char*)scratch;
+    qg_half* norm = (qg_half*)(base + L.norm);
+    qg_half* qkv = (qg_half*)(base + L.qkv);
+    qg_half* u = (qg_half*)(base + L.u);
+    qg_half* y = (qg_half*)(base + L.y);
+    void* ws = base + L.ws;
+    const int D = blk->D, F = blk->F;
+    hipError_t e = hipSuccess;
+    // At M == 1 the QKV and up GEMVs compute the LayerNorm of h in their
+    // prologue (the up GEMV also stores it as the scratch norm); otherwise a
+    // LayerNorm kernel writes norm first.
+    const bool fuse_qkv = qg::gemm_fuses_layernorm(blk->qkv.bits, M, D, 3 * D);
+    const bool fuse_up = qg::gemm_fuses_layernorm(blk->up.bits, M, D, F);
+    for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
+        qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
+        if (fuse_qkv)
+            qa.ln_h = h;
+        else
+            e = qg::launch_layernorm(h, M, D, norm, s);
+        if (e == hipSuccess) e = qg::launch_gemm(qa, s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({qkv + 2 * D, 3 * D, &blk->out, y, D, M, qg::kResidual, h, D, ws,
+                                 L.ws_bytes},
+                                s);
+        qg::GemmArgs ua{norm, D, &blk->up, u, F, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
+        if (fuse_up) {
+            ua.ln_h = h;
+            ua.norm_out = norm;
+        } else if (e == hipSuccess) {
+            e = qg::launch_layernorm(h, M, D, norm, s);
+        }
+        if (e == hipSuccess) e = qg::launch_gemm(ua, s);
+        if (e == hipSuccess)
+            e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
+                                s);
+    }
+    return e;
+}
+
+// QG_LOOP_GRAPHS=0 makes qg_loop_range enqueue kernels one by one (debugging
+// and the graph-versus-direct parity test); read on every call.
+bool loop_graphs_enabled() {
+    const char* v = getenv("QG_LOOP_GRAPHS");
+    return !(v && v[0] == '0');
+}
+
+// Cached, instantiated graphs of the loop's kernel sequence.  A graph bakes in
+// every pointer and shape it was built with, so the key holds all of them.
+struct LoopKey {
+    qg_block blk;
+    const float* h;
+    void* scratch;
+    int32_t M, iters, device;
+    bool operator==(const LoopKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
+};
+
+struct LoopGraph {
+    LoopKey key;
+    hipGraphExec_t exec;
+    uint64_t last_use;
+};
+
+std::mutex g_graph_mu;
+std::vector<LoopGraph> g_graphs;
+uint64_t g_graph_clock = 0;
+hipStream_t g_capture_stream[64] = {nullptr};
+constexpr size_t kMaxGraphs = 32;
+
+hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
+                      const LoopLayout& L, hipGraphExec_t* out) {
+    LoopKey key;
+    memset(&key, 0, sizeof key);  // padding takes part in the comparison
+    key.blk = *blk;
+    key.h = h;
+    key.scratch = scratch;
+    key.M = M;
+    key.iters = iters;
+    hipError_t e = hipGetDevice(&key.device);
+    if (e != hipSuccess) return e;
+    if (key.device < 0 || key.device >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_graph_mu);
+    for (LoopGraph& g : g_graphs) {
+        if (g.key == key) {
+            g.last_use = ++g_graph_clock;
+            *out = g.exec;
+            return hipSuccess;
+        }
+    }
+    hipStream_t& cs = g_capture_stream[key.device];
+    if (!cs && (e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking)) != hipSuccess) {
+        cs = nullptr;
+        return e;
+    }
+    if ((e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    if (le != hipSuccess || e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return le != hipSuccess ? le : e;
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return e;
+    if (g_graphs.size() >= kMaxGraphs) {
+        // Evict the least recently used graph; a graph already launched on a
+        // stream stays valid until that launch completes, so sync first.
+        size_t lru = 0;
+        for (size_t i = 1; i < g_graphs.size(); ++i)
+            if (g_graphs[i].last_use < g_graphs[lru].last_use) lru = i;
+        (void)hipDeviceSynchronize();
+        (void)hipGraphExecDestroy(g_graphs[lru].exec);
+        g_graphs.erase(g_graphs.begin() + lru);
+    }
+    g_graphs.push_back({key, exec, ++g_graph_clock});
+    *out = exec;
+    return hipSuccess;
+}
+
 // Per-device status word for qg_pack (library-owned, freed by qg_release_cache).
 std::mutex g_pack_mu;
 int* g_pack_status[64] = {nullptr};
@@ -256,32 +382,18 @@ int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t 
         return fail(QG_EINVAL, "%s: scratch of %zu bytes is smaller than the %zu required", fn,
                     scratch_bytes, L.total);
     hipStream_t s = (hipStream_t)stream;
-    char* base = (char*)scratch;
-    qg_half* norm = (qg_half*)(base + L.norm);
-    qg_half* qkv = (qg_half*)(base + L.qkv);
-    qg_half* u = (qg_half*)(base + L.u);
-    qg_half* y = (qg_half*)(base + L.y);
-    void* ws = base + L.ws;
-    const int D = blk->D, F = blk->F;
     hipError_t e = hipSuccess;
-    for (int32_t l = L0; l < L1 && e == hipSuccess; ++l) {
-        e = qg::launch_layernorm(h, M, D, norm, s);
-        if (e == hipSuccess)
-            e = qg::launch_gemm({norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws,
-                                 L.ws_bytes},
-                                s);
-        if (e == hipSuccess)
-            e = qg::launch_gemm({qkv + 2 * D, 3 * D, &blk->out, y, D, M, qg::kResidual, h, D, ws,
-                                 L.ws_bytes},
-                                s);
-        if (e == hipSuccess) e = qg::launch_layernorm(h, M, D, norm, s);
-        if (e == hipSuccess)
-            e = qg::launch_gemm({norm, D, &blk->up, u, F, M, qg::kStore, nullptr, 0, ws,
-                                 L.ws_bytes},
-                                s);
-        if (e == hipSuccess)
-            e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
-                                s);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return hip_fail(fn, e);
+    // Inside a caller's graph capture, or with graphs switched off, the
+    // kernels are enqueued one by one; otherwise the iteration sequence is
+    // replayed from a cached graph (one launch instead of 4-6 per iteration).
+    if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled()) {
+        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, s);
+    } else {
+        hipGraphExec_t exec = nullptr;
+        e = loop_graph(blk, h, M, L1 - L0, scratch, L, &exec);
+        if (e == hipSuccess) e = hipGraphLaunch(exec, s);
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
@@ -306,6 +418,14 @@ int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream) {
 }
 
 void qg_release_cache(void) {
+    {
+        std::lock_guard<std::mutex> glock(g_graph_mu);
+        if (!g_graphs.empty()) {
+            (void)hipDeviceSynchronize();
+            for (LoopGraph& g : g_graphs) (void)hipGraphExecDestroy(g.exec);
+            g_graphs.clear();
+        }
+    }
     std::lock_guard<std::mutex> lock(g_pack_mu);
     bool any = false;
     for (int* p : g_pack_status) any |= p != nullptr;

@@ -77,6 +77,8 @@ def lib():
         for name in ("or_round_half_array", "or_half_to_double_array"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [vp, i64, vp]
+        L.or_num_threads.restype = C.c_int
+        L.or_num_threads.argtypes = []
         L.or_half_bits_array.restype = None
         L.or_half_bits_array.argtypes = [vp, i64, vp]
         _lib = L
@@ -97,6 +99,11 @@ class OracleError(RuntimeError):
 def _check(fn: str, st: int):
     if st != OK:
         raise OracleError(fn, st)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS or all cores)."""
+    return lib().or_num_threads()
 
 
 # ------------------------------------------------------------------ FP16 ----

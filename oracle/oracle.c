@@ -37,6 +37,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -429,4 +430,10 @@ void or_half_to_double_array(const uint16_t* h, int64_t n, double* out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_half_to_double(h[i]);
+}
+
+/* Threads the oracle's OpenMP loops use (reported beside its timings). */
+int or_num_threads(void)
+{
+    return omp_get_max_threads();
 }

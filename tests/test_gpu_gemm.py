@@ -167,3 +167,24 @@ def test_gemm_rejects_mismatched_bits():
     p = qg.qg_pack(W.cuda(), 4)
     with pytest.raises(qg.QGValueError):
         qg.qg_gemm_int2(X.cuda(), p)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_gemm_captured_in_graph_replays(M):
+    """GEMM launches recorded in a caller's graph (as the bench does) replay to
+    the eager result every time, with eager work between replays."""
+    W, X = workloads.single_gemm(M, 2048, 512, seed=4)
+    p = qg.qg_pack(W.cuda(), 4)
+    Xd = X.cuda()
+    ref = f16_bits(qg.qg_gemm_int4(Xd, p))
+    Y = torch.empty(M, 512, dtype=torch.float16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qg.qg_gemm_int4(Xd, p, Y=Y)
+    for r in range(3):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(f16_bits(Y), ref), f"replay {r}"
+        qg.qg_gemm_int4(Xd[:1], p)
+        torch.cuda.synchronize()

@@ -92,3 +92,51 @@ def test_loop_measured_workloads_sampled_rows(orc, name, bits, M, L, rows):
     href, last = orc.loop_range(oblk, inp.X.numpy()[rows].astype(np.float64), 0, L)
     _check_h(h[rows], href, name)
     _check_scratch(qg.scratch_views(blk, M, scratch), last, rows, name)
+
+
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_loop_graph_replays_match_direct_enqueue(orc, M, monkeypatch):
+    """The cached-graph path and the kernel-by-kernel path give the same bits;
+    every replay is checked, with eager library work and syncs in between."""
+    D, F = 256, 512
+    inp, blk, _ = _blocks(orc, M, 4, D, F, seed=21)
+    h0 = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
+    ref = h0.clone()
+    qg.qg_loop_range(blk, ref, 0, 3, scratch)
+    torch.cuda.synchronize()
+    h = torch.empty_like(h0)
+    for r in range(4):
+        monkeypatch.setenv("QG_LOOP_GRAPHS", "1")
+        h.copy_(h0)
+        qg.qg_loop_range(blk, h, 0, 3, scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref), f"graph replay {r} differs from direct enqueue"
+        monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
+        other = h0.clone()
+        qg.qg_loop_range(blk, other, 0, 1, scratch)   # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_loop_inside_caller_graph_capture(orc):
+    """Under a caller's stream capture the kernels are recorded into the
+    caller's graph; each replay must equal the eager result."""
+    D, F, M = 256, 512, 1
+    inp, blk, _ = _blocks(orc, M, 4, D, F, seed=22)
+    h0 = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    ref = h0.clone()
+    qg.qg_loop_range(blk, ref, 0, 2, scratch)
+    h = h0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qg.qg_loop_range(blk, h, 0, 2, scratch)
+    for r in range(3):
+        h.copy_(h0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref), f"captured replay {r}"
+        tmp = h0.clone()
+        qg.qg_loop_range(blk, tmp, 0, 1, scratch)
+        torch.cuda.synchronize()
