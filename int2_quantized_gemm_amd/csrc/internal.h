@@ -50,6 +50,8 @@ enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };
 GemmPath gemm_path(int bits, int M, int K, int N);
 size_t gemm_ws_bytes(int bits, int M, int K, int N);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// M > 16: LDS-staged, double-buffered MFMA GEMM (kernels_prefill.hip).
+hipError_t launch_prefill(const GemmArgs& a, hipStream_t s);
 
 // ---- loop glue (kernels_loop.hip)
 // norm[m][:] = fp16(LN(h[m][:])), parameter-free, eps 1e-5, FP32.

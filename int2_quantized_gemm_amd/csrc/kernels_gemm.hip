@@ -573,7 +573,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     switch (gemm_path(bits, a.M, a.w->K, a.w->N)) {
         case kPathGemv: return bits == 4 ? launch_gemv<4>(a, s) : launch_gemv<2>(a, s);
         case kPathSkinny: return bits == 4 ? launch_skinny<4>(a, s) : launch_skinny<2>(a, s);
-        default: return bits == 4 ? launch_tiled<4>(a, s) : launch_tiled<2>(a, s);
+        default: return launch_prefill(a, s);
     }
 }
 
