@@ -50,8 +50,10 @@ enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };
 GemmPath gemm_path(int bits, int M, int K, int N);
 size_t gemm_ws_bytes(int bits, int M, int K, int N);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
-// M > 16: LDS-staged, double-buffered MFMA GEMM (kernels_prefill.hip).
+// M > 16: LDS-staged, double-buffered MFMA GEMM (kernels_prefill.hip); when it
+// splits K, a.ws must hold prefill_ws_bytes(M, N, K) bytes of FP32 partials.
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t s);
+size_t prefill_ws_bytes(int M, int N, int K);
 
 // ---- loop glue (kernels_loop.hip)
 // norm[m][:] = fp16(LN(h[m][:])), parameter-free, eps 1e-5, FP32.

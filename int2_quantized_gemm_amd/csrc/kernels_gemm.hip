@@ -15,8 +15,7 @@
 //     workgroup, K split over the workgroup's waves and reduced through LDS in
 //     wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A (M padded to 16)
 //     and dequantised weights as B.
-//   * k_gemm_tiled (M > 16): 128x128 output tiles, 2x2 waves of 64x64, the
-//     same MFMA; weights dequantised to FP16 (one rounding of (q - z) * s).
+//   * M > 16: the LDS-staged MFMA GEMM of kernels_prefill.hip.
 //
 // MFMA operand mapping used everywhere (16x16x32 f16): lane l supplies row
 // (A) or column (B) l % 16 and eight k values selected by l / 16; A and B use
@@ -358,90 +357,6 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_gemm_skinny(
     }
 }
 
-// ----------------------------------------------------------------- tiled ----
-
-template <int BITS>
-__global__ __launch_bounds__(256) void k_gemm_tiled(
-    const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi) {
-    using F = Fmt<BITS>;
-    constexpr int WM = 4, WN = 4;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nl = lane & 15, c = lane >> 4;
-    const int m_base = blockIdx.y * 128 + (wave >> 1) * 64;
-    const int n_base = blockIdx.x * 128 + (wave & 1) * 64;
-    const int groups = K / kGroup;
-    const int wpr = K / F::kCodesPerWord;
-
-    const uint32_t* crow[WN];
-    bool nvalid[WN];
-    int nrow[WN];
-#pragma unroll
-    for (int jn = 0; jn < WN; ++jn) {
-        nrow[jn] = n_base + 16 * jn + nl;
-        nvalid[jn] = nrow[jn] < N;
-        crow[jn] = codes + (int64_t)(nvalid[jn] ? nrow[jn] : 0) * wpr;
-    }
-    const uint16_t* xrow[WM];
-    bool mvalid[WM];
-#pragma unroll
-    for (int im = 0; im < WM; ++im) {
-        const int m = m_base + 16 * im + nl;
-        mvalid[im] = m < M;
-        xrow[im] = X + (int64_t)(mvalid[im] ? m : 0) * ldx;
-    }
-
-    f32x4 acc[WM][WN];
-#pragma unroll
-    for (int im = 0; im < WM; ++im)
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) acc[im][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int g = 0; g < groups; ++g) {
-        LaneCodes<BITS> lc[WN];
-        GroupConst gc[WN];
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-            uint16_t sb = 0, zb = 0;
-            if (nvalid[jn]) {
-                lc[jn].load(crow[jn], g, c);
-                sb = scales[(int64_t)nrow[jn] * groups + g];
-                zb = zeros[(int64_t)nrow[jn] * groups + g];
-            } else {
-                lc[jn].zero();
-            }
-            gc[jn] = group_const(sb, zb);
-        }
-        f16x8 a[WM][4];
-#pragma unroll
-        for (int im = 0; im < WM; ++im) load_a(xrow[im], mvalid[im], g, c, a[im]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f16x8 b[WN];
-#pragma unroll
-            for (int jn = 0; jn < WN; ++jn) b[jn] = lc[jn].frag(j, gc[jn]);
-#pragma unroll
-            for (int im = 0; im < WM; ++im)
-#pragma unroll
-                for (int jn = 0; jn < WN; ++jn) acc[im][jn] = mfma16(a[im][j], b[jn], acc[im][jn]);
-        }
-    }
-
-#pragma unroll
-    for (int im = 0; im < WM; ++im)
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-            if (!nvalid[jn]) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m_base + 16 * im + 4 * c + r;
-                if (m < M) store_out(Y, ldy, h, ldh, epi, m, nrow[jn], acc[im][jn][r]);
-            }
-        }
-}
-
 // ------------------------------------------------------------ dispatch ----
 
 struct GemvShape {
@@ -538,15 +453,6 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
-    dim3 grid((a.w->N + 127) / 128, (a.M + 127) / 128);
-    k_gemm_tiled<BITS><<<grid, 256, 0, s>>>(a.X, a.ldx, a.M, a.w->codes, a.w->scales,
-                                             a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h, a.ldh,
-                                             (int)a.epi);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 GemmPath gemm_path(int bits, int M, int K, int N) {
@@ -561,11 +467,7 @@ bool gemm_fuses_layernorm(int bits, int M, int K, int N) {
 }
 
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {
-    (void)bits;
-    (void)M;
-    (void)K;
-    (void)N;
-    return 0;
+    return gemm_path(bits, M, K, N) == kPathTiled ? prefill_ws_bytes(M, N, K) : 0;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

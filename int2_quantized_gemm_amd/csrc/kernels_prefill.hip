@@ -75,7 +75,8 @@ template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int ST
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefill(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi) {
+    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
+    int groups_per_part, float* __restrict__ part) {
     using C = Cfg<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES>;
     __shared__ __attribute__((aligned(16))) f16 lds[C::LDS_HALVES];
 
@@ -90,6 +91,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     const int n0 = blockIdx.x * BN;
     const int groups = K / kBK;
     const int wpr = K / Fmt<BITS>::kCodesPerWord;
+    // K split: workgroup z covers groups [g_lo, g_lo + groups_per_part) and,
+    // when `part` is set, writes its FP32 partial tile to part[z][M][N].
+    const int g_lo = blockIdx.z * groups_per_part;
+    const int g_n = groups_per_part;
 
     // Block-relative buffer resources (offsets stay far below 2^31).
     const __amdgpu_buffer_rsrc_t ra =
@@ -191,13 +196,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
         }
     };
 
-    load(0);
+    load(g_lo);
 #pragma unroll
     for (int p = 0; p < 4; ++p) store_piece(0, p);
     __syncthreads();
-    for (int g = 0; g < groups; ++g) {
-        const bool more = g + 1 < groups;
-        if (more) load(g + 1);
+    for (int g = 0; g < g_n; ++g) {
+        const bool more = g + 1 < g_n;
+        if (more) load(g_lo + g + 1);
         if constexpr (STAGES == 2) {
             const int cur = g & 1;
             // four quarters of the step's eight k-slices; the next stage's
@@ -226,6 +231,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     auto emit = [&](int im, int jn, const f32x16& v) {
         const int n = n0 + wn * C::WTN + 32 * jn + l32;
         if (n >= N) return;
+        if (part != nullptr) {
+            float* pz = part + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * C::WTM + 32 * im + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (m < M) pz[(int64_t)m * N + n] = v[r];
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * C::WTM + 32 * im + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -266,34 +280,96 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     }
 }
 
-template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int STAGES,
-          int STORE_FROM>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-    dim3 grid((a.w->N + BN - 1) / BN, (a.M + BM - 1) / BM);
-    constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
-    k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
-        a.ldh, (int)a.epi);
-    return hipGetLastError();
+// Sum of the K-split partial tiles part[0..S)[M][N] in split order, rounded to
+// FP16, with the optional residual epilogue.  Four elements per thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
+                                                       int M, int N, uint16_t* __restrict__ Y,
+                                                       int64_t ldy, float* __restrict__ h,
+                                                       int64_t ldh, int epi) {
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int64_t total = (int64_t)M * N;
+    if (i4 >= total) return;
+    const int64_t plane = total;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i4 + e;
+        if (i >= total) break;
+        float v = part[i];
+        for (int z = 1; z < S; ++z) v += part[z * plane + i];
+        const int64_t m = i / N, n = i % N;
+        const uint16_t y = f32_to_f16_bits(v);
+        Y[m * ldy + n] = y;
+        if (epi == kResidual) h[m * ldh + n] += (float)as_f16(y);
+    }
 }
+
+struct Plan {
+    int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64
+    int split;  // K parts
+};
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Tile choice, from a sweep on MI355X: with at least two 128x128 tiles per CU,
 // single-stage 128x128 workgroups (two resident per CU overlap each other's
 // barriers); with about one per CU, 128x128 on eight waves splitting each
 // step's k-slices in two; with fewer tiles, 64x64 workgroups of four 32x32
-// waves, several resident per CU.
+// waves, several resident per CU.  When even that leaves CUs idle, K is split
+// over up to 8 parts of at least 4 groups (512 values) each.
+Plan plan_for(int M, int N, int K) {
+    const int groups = K / kBK;
+    const int t128 = ceil_div(M, 128) * ceil_div(N, 128);
+    const int t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    if (t128 >= 512) return {0, 1};
+    if (t128 >= 240) return {1, 1};
+    auto best_split = [&](int tiles) {
+        int sp = 1;
+        while (sp < 8 && tiles * sp < 240 && groups % (2 * sp) == 0 && groups / (2 * sp) >= 4) sp *= 2;
+        return sp;
+    };
+    const int s128 = best_split(t128);
+    if (t128 * s128 >= 240 && groups / s128 >= 16) return {1, s128};
+    if (t64 >= 240) return {2, 1};
+    return {2, best_split(t64)};
+}
+
+template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int STAGES,
+          int STORE_FROM>
+hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
+    dim3 grid((a.w->N + BN - 1) / BN, (a.M + BM - 1) / BM, split);
+    constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
+    float* part = split > 1 ? (float*)a.ws : nullptr;
+    k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
+        a.ldh, (int)a.epi, a.w->K / kBK / split, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || split == 1) return e;
+    const int64_t total = (int64_t)a.M * a.w->N;
+    const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
+    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, split, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
+                                           (int)a.epi);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
-    const int64_t big_tiles = (int64_t)((a.w->N + 127) / 128) * ((a.M + 127) / 128);
-    if (big_tiles >= 512) return launch_cfg<BITS, 128, 128, 2, 2, 1, 1, 0>(a, s);
-    if (big_tiles >= 240) return launch_cfg<BITS, 128, 128, 2, 2, 2, 2, 2>(a, s);
-    return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, s);
+    const Plan p = plan_for(a.M, a.w->N, a.w->K);
+    switch (p.cfg) {
+        case 0: return launch_cfg<BITS, 128, 128, 2, 2, 1, 1, 0>(a, p.split, s);
+        case 1: return launch_cfg<BITS, 128, 128, 2, 2, 2, 2, 2>(a, p.split, s);
+        default: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t s) {
     return a.w->bits == 4 ? launch_bits<4>(a, s) : launch_bits<2>(a, s);
+}
+
+size_t prefill_ws_bytes(int M, int N, int K) {
+    const Plan p = plan_for(M, N, K);
+    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
 }
 
 }  // namespace qg

@@ -68,7 +68,7 @@ int check_weight(const qg_weight* w, const char* fn, const char* name) {
 }
 
 int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half* Y, int64_t ldy,
-               int32_t M, size_t ws_bytes, int bits, const char* fn) {
+               int32_t M, const void* ws, size_t ws_bytes, int bits, const char* fn) {
     int st = check_weight(w, fn, "w");
     if (st) return st;
     if (w->bits != bits)
@@ -89,6 +89,8 @@ int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half*
     if (ws_bytes < need)
         return fail(QG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
                     ws_bytes, need);
+    if (need > 0 && !aligned(ws, 16))
+        return fail(QG_EINVAL, "%s: workspace must be a 16-byte aligned pointer", fn);
     return QG_OK;
 }
 
@@ -328,7 +330,7 @@ size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M) {
 static int gemm_entry(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
                       int32_t M, void* ws, size_t ws_bytes, void* stream, int bits,
                       const char* fn) {
-    int st = check_gemm(X, ldx, w, Y, ldy, M, ws_bytes, bits, fn);
+    int st = check_gemm(X, ldx, w, Y, ldy, M, ws, ws_bytes, bits, fn);
     if (st) return st;
     if (M == 0) return ok();
     qg::GemmArgs a{X, ldx, w, Y, ldy, M, qg::kStore, nullptr, 0, ws, ws_bytes};
