@@ -307,7 +307,13 @@ __device__ __forceinline__ void store_out(uint16_t* Y, int64_t ldy, float* h, in
 
 // ---------------------------------------------------------------- skinny ----
 
-template <int BITS, int KSPLIT>
+// 16 output channels per workgroup, K split over KSPLIT waves, each wave
+// owning at most GPW groups.  All loads of a wave (codes, scales, zeros and
+// the 16 activation rows of its k range) are issued before its first MFMA,
+// so the wave pays one memory latency.  Rows past N or M are clamped for the
+// loads and zeroed by value (scale 0, activation 0): no branches around loads.
+// The KSPLIT partial tiles are summed through LDS in wave order.
+template <int BITS, int KSPLIT, int GPW>
 __global__ __launch_bounds__(64 * KSPLIT) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
@@ -319,29 +325,37 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_gemm_skinny(
     const int nl = lane & 15, c = lane >> 4;
     const int n = blockIdx.x * 16 + nl;
     const bool nvalid = n < N;
-    const bool mvalid = nl < M;  // A row of this lane
+    const bool mvalid = nl < M;
     const int groups = K / kGroup;
     const int g0 = (int)((int64_t)groups * wave / KSPLIT);
-    const int g1 = (int)((int64_t)groups * (wave + 1) / KSPLIT);
-    const uint32_t* crow = codes + (int64_t)(nvalid ? n : 0) * (K / F::kCodesPerWord);
-    const uint16_t* xrow = X + (int64_t)(mvalid ? nl : 0) * ldx;
+    const int gn = (int)((int64_t)groups * (wave + 1) / KSPLIT) - g0;  // <= GPW
+    const int nr = nvalid ? n : N - 1;
+    const uint32_t* crow = codes + (int64_t)nr * (K / F::kCodesPerWord);
+    const uint16_t* xrow = X + (int64_t)(mvalid ? nl : M - 1) * ldx;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int g = g0; g < g1; ++g) {
-        LaneCodes<BITS> lc;
-        uint16_t sb = 0, zb = 0;
-        if (nvalid) {
-            lc.load(crow, g, c);
-            sb = scales[(int64_t)n * groups + g];
-            zb = zeros[(int64_t)n * groups + g];
-        } else {
-            lc.zero();
-        }
-        f16x8 a[4];
-        load_a(xrow, mvalid, g, c, a);
-        const GroupConst gc = group_const(sb, zb);
+    LaneCodes<BITS> lc[GPW];
+    uint16_t sb[GPW], zb[GPW];
+    f16x8 a[GPW][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma16(a[j], lc.frag(j, gc), acc);
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + (i < gn ? i : 0);  // spare slots reload group g0 (unused)
+        lc[i].load(crow, g, c);
+        sb[i] = scales[(int64_t)nr * groups + g];
+        zb[i] = zeros[(int64_t)nr * groups + g];
+        const f16x8* p = (const f16x8*)(xrow + g * kGroup + c * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[i][j] = p[j];
+    }
+    const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        if (i < gn) {
+            const GroupConst gc = group_const(nvalid ? sb[i] : (uint16_t)0, zb[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc = mfma16(mvalid ? a[i][j] : zero8, lc[i].frag(j, gc), acc);
+        }
     }
     red[wave][lane] = acc;
     __syncthreads();
@@ -443,13 +457,25 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
     return a.ln_h ? launch_gemv_ln<BITS, true>(a, s) : launch_gemv_ln<BITS, false>(a, s);
 }
 
+// K split so that each wave owns at most 4 groups: 4 waves up to K = 2048,
+// 8 up to 4096, 16 up to 8192.
 template <int BITS>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-    constexpr int KSPLIT = 4;
+    const int groups = a.w->K / kGroup;
     const int blocks = (a.w->N + 15) / 16;
-    k_gemm_skinny<BITS, KSPLIT><<<blocks, 64 * KSPLIT, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
-        a.ldh, (int)a.epi);
+#define QG_SKINNY(KS, GPW)                                                                      \
+    k_gemm_skinny<BITS, KS, GPW><<<blocks, 64 * KS, 0, s>>>(                                    \
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h, \
+        a.ldh, (int)a.epi)
+    if (groups <= 16)
+        QG_SKINNY(4, 4);
+    else if (groups <= 32)
+        QG_SKINNY(8, 4);
+    else if (groups <= 64)
+        QG_SKINNY(16, 4);
+    else
+        return hipErrorInvalidValue;  // not dispatched: gemm_path sends K > 8192 to the tiled path
+#undef QG_SKINNY
     return hipGetLastError();
 }
 
@@ -458,7 +484,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 GemmPath gemm_path(int bits, int M, int K, int N) {
     (void)N;
     if (M == 1 && gemv_shape(bits, K).ok) return kPathGemv;
-    if (M <= 16) return kPathSkinny;
+    if (M <= 16 && K <= 8192) return kPathSkinny;
     return kPathTiled;
 }
 
