@@ -26,6 +26,8 @@
 #include "device.h"
 #include "internal.h"
 
+#include <utility>
+
 namespace qg {
 namespace {
 
@@ -280,6 +282,362 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     }
 }
 
+// Buffer descriptor as four SGPRs (base, no stride, num_records bytes, raw
+// buffer flags as for make_rsrc), for the inline-asm LDS DMA below.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc_sgpr(const void* base, int64_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    const int32_t n = bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)(bytes < 0 ? 0 : bytes);
+    return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
+                 __builtin_amdgcn_readfirstlane((int32_t)((b >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(n), 0x00020000};
+}
+
+// One 16-byte-per-lane buffer load written straight to LDS (lane l's bytes
+// land at lds + 16 l; the wave's LDS base goes through M0, which an LDS DMA
+// may read only one wait state after the SALU write).  Issued as inline
+// asm so that the compiler does not wait for it before unrelated LDS reads:
+// completion is the caller's business (wait_vmcnt, then a barrier).  Out of
+// range offsets read as zero.
+__device__ __forceinline__ void dma16(i32x4 rsrc, const void* lds, uint32_t voffset) {
+    const int32_t m0 = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Workgroup barrier for LDS producers/consumers whose vector-memory waits are
+// explicit: finishes this wave's LDS accesses, then s_barrier.  The asm
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most c (runtime, 0 <= c) vector-memory operations are
+// pending; c >= N is treated as N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int c) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (c >= N)
+            wait_vmcnt<N>();
+        else
+            wait_vmcnt_le<N - 1>(c);
+    }
+}
+
+// 32-bit constants in registers the compiler cannot fold (an SGPR and a
+// VGPR), so that a mask and an OR constant meet in one fused VOP3 instruction
+// (v_and_or / v_bitop3), which can take neither a literal nor two SGPRs.
+__device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
+// ---- Deep-prefetch variant ("ring").  Every operand of a step reaches LDS by
+// LDS DMA (buffer_load_dwordx4 ... lds), issued ahead into rings of stages,
+// so global latency is hidden without holding data in registers and without
+// the compiler's conservative waits on register loads.  The A tile (reused by
+// many workgroups, mostly an L2 hit) is issued RA-1 steps ahead; the packed
+// codes, scales and zeros (read by few workgroups, mostly from HBM with its
+// longer latency) RB-1 steps ahead.  Each step a wave waits for its own DMAs
+// of that step (s_waitcnt vmcnt with the exact count of later DMAs left
+// outstanding), then one barrier publishes all waves' data and frees the
+// stages read in the previous step.
+//
+// Stage layout, in 16-byte units:
+//   A: BM rows x 16 chunks; chunk c of row r at unit 16 r + (c ^ (r % 16)), so
+//      the fragment reads of 16 consecutive rows hit distinct banks;
+//   B: 128 columns x CH chunks (CH = 4 for INT4, 2 for INT2) of the packed
+//      codes of one group; chunk q of column n at unit CH n + (q ^ swz(n)),
+//      again so that 16 consecutive columns read distinct banks.
+// Scales and zeros come 8 groups at a time (16 contiguous bytes per column)
+// into a double buffer.
+//
+// The four waves each own a 32-column strip of the 128-wide tile (TM = BM/32
+// MFMA tiles of 32 x 32 down it), so a wave dequantises each B fragment once
+// and feeds it to TM MFMAs; that keeps the dequantisation at under 4 VALU
+// instructions per MFMA, which a wave's VALU work still overlaps with its
+// own MFMAs (measured; a 2 x 2 wave grid, which halves the LDS reads but
+// doubles the dequantisation, was slower).  Lane l takes column l % 32 of the
+// strip and the k run [64 h, 64 h + 64) of a step (h = l / 32), slice j the
+// j-th 8 of that run, and reads A fragments with the same assignment, one
+// slice ahead of the MFMAs.
+template <int BITS>
+struct RingB {
+    static constexpr int CH = BITS == 4 ? 4 : 2;  // 16-byte chunks per column and group
+    static constexpr int BYTES = 128 * CH * 16;
+    __device__ static int swz(int n) { return BITS == 4 ? (n >> 2) & 3 : (n >> 3) & 1; }
+};
+
+// The ring kernel needs 16-byte aligned DMA sources and runs of 8 groups of
+// scales that stay inside one K part.
+bool ring_ok(const GemmArgs& a, int split) {
+    const int groups = a.w->K / kBK;
+    return groups % split == 0 && (groups / split) % 8 == 0 && (a.ldx % 8) == 0 &&
+           ((uintptr_t)a.X % 16) == 0 && ((uintptr_t)a.w->codes % 16) == 0 &&
+           ((uintptr_t)a.w->scales % 16) == 0 && ((uintptr_t)a.w->zeros % 16) == 0;
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// XCD-aware order of output tiles.  Workgroup i of a launch runs on XCD
+// i mod 8, and each XCD has its own L2, so the tiles of one XCD should share
+// operands: the gx x gy tile grid is cut into rx x ry sub-grids of sx x sy
+// tiles (rx ry = 8), sub-grid c for XCD c.  Each A row-block is then fetched
+// into rx L2s and each B column-block into ry, instead of up to 8 each; the
+// host picks (rx, ry) for the least total.  The launch has 8 sx sy
+// workgroups; those past the grid's edge exit at once.
+struct Raster {
+    int gx, gy, rx, sx, sy;
+    __device__ bool tile(int i, int& tx, int& ty) const {
+        const int xcd = i & 7, slot = i >> 3;
+        tx = (xcd % rx) * sx + slot % sx;
+        ty = (xcd / rx) * sy + slot / sx;
+        return tx < gx && ty < gy;
+    }
+};
+
+// Choose the raster for a gx x gy grid whose A row-blocks are a_bytes each
+// and B column-blocks b_bytes each.
+Raster make_raster(int gx, int gy, double a_bytes, double b_bytes) {
+    Raster best{gx, gy, 8, 1, 1};
+    double best_cost = -1.0;
+    for (int rx = 1; rx <= 8; rx *= 2) {
+        const int ry = 8 / rx;
+        const int sx = (gx + rx - 1) / rx, sy = (gy + ry - 1) / ry;
+        const double idle = 8.0 * sx * sy - (double)gx * gy;
+        // fetches: each of gy row-blocks into min(rx, gx) L2s, each of gx
+        // column-blocks into min(ry, gy); idle slots cost a wave of tiles
+        const double cost = gy * a_bytes * (rx < gx ? rx : gx) + gx * b_bytes * (ry < gy ? ry : gy) +
+                            idle * (a_bytes + b_bytes);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = Raster{gx, gy, rx, sx, sy};
+        }
+    }
+    return best;
+}
+
+// f(integral_constant<int, i>) for i = 0 .. n-1, in order (compile-time i).
+template <class Fn, int... Is>
+__device__ __forceinline__ void for_each_index(Fn&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+
+template <int BITS, int BM, int RA, int RBS>
+__global__ __launch_bounds__(256) void k_gemm_ring(
+    const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
+    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
+    int groups_per_part, float* __restrict__ part, Raster rs) {
+    using F = Fmt<BITS>;
+    using RB = RingB<BITS>;
+    constexpr int TM = BM / 32;
+    constexpr int A_BYTES = BM * kBK * 2;
+    constexpr int A_DMA = A_BYTES / 1024 / 4;    // A instructions per wave and step
+    constexpr int B_DMA = RB::BYTES / 1024 / 4;  // B instructions per wave and step
+    constexpr int CH = RB::CH;
+    constexpr int LANE_WORDS = 64 / F::kCodesPerWord;  // packed words of a lane's k run
+    constexpr int U = RA * RBS / gcd_c(RA, RBS);       // steps per unrolled round
+    static_assert(RA >= 2 && RBS > RA && RBS <= 9, "stage counts");
+    static_assert(A_DMA >= 1 && B_DMA >= 1, "whole DMA instructions per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a[RA][A_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b[RBS][RB::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_sz[2][2][128 * 16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    int tx, ty;
+    if (!rs.tile(blockIdx.x, tx, ty)) return;  // padding workgroup of the raster
+    const int m0 = ty * BM;
+    const int n0 = tx * 128;
+    const int groups = K / kBK;
+    const int wpr = K / F::kCodesPerWord;
+    const int g_lo = blockIdx.z * groups_per_part;
+    const int G = groups_per_part;
+
+    const i32x4 ra =
+        make_rsrc_sgpr(X + (int64_t)m0 * ldx, ((int64_t)(M - m0 - 1) * ldx + K) * 2);
+    const i32x4 rb = make_rsrc_sgpr(codes + (int64_t)n0 * wpr, (int64_t)(N - n0) * wpr * 4);
+    // Waves 0, 1 load scales and waves 2, 3 zeros, of columns 64 (w % 2) + lane.
+    const i32x4 rsz = make_rsrc_sgpr((wave < 2 ? scales : zeros) + (int64_t)n0 * groups,
+                                     (int64_t)(N - n0) * groups * 2);
+
+    // Source offsets of this lane's DMA slots at step 0 of the part.
+    uint32_t a_off[A_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int unit = (wave * A_DMA + i) * 64 + lane;
+        const int row = unit >> 4;
+        const int c = (unit & 15) ^ (row & 15);
+        a_off[i] = (uint32_t)((row * ldx + (int64_t)g_lo * kBK + c * 8) * 2);
+    }
+    uint32_t b_off[B_DMA];
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const int unit = (wave * B_DMA + i) * 64 + lane;
+        const int n = unit / CH;
+        const int q = (unit % CH) ^ RB::swz(n);
+        b_off[i] = (uint32_t)(n * wpr * 4 + g_lo * F::kWordsPerGroup * 4 + q * 16);
+    }
+    const uint32_t sz_off = (uint32_t)((((wave & 1) * 64 + lane) * groups + g_lo) * 2);
+
+    // Iteration t issues A of step t + RA - 1, then B (and, every 8 steps,
+    // the scales and zeros of the next 8) of step t + RB - 1.
+    auto issue = [&](int t) {
+        const int sa = t + RA - 1;
+        if (sa >= 0 && sa < G) {
+            uint8_t* dst = lds_a[sa % RA] + wave * A_DMA * 1024;
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i) dma16(ra, dst + i * 1024, a_off[i] + sa * kBK * 2);
+        }
+        const int sb = t + RBS - 1;
+        if (sb >= 0 && sb < G) {
+            uint8_t* dst = lds_b[sb % RBS] + wave * B_DMA * 1024;
+#pragma unroll
+            for (int i = 0; i < B_DMA; ++i)
+                dma16(rb, dst + i * 1024, b_off[i] + sb * F::kWordsPerGroup * 4);
+            if ((sb & 7) == 0)
+                dma16(rsz, &lds_sz[(sb >> 3) & 1][wave >> 1][(wave & 1) * 1024], sz_off + sb * 2);
+        }
+    };
+
+    f32x16 acc[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tm][r] = 0.0f;
+
+    // Per-lane LDS byte offsets within a stage: the A fragment of slice j for
+    // tile row 0 (tile row tm adds 32 rows, 8 KiB), the B codes of this
+    // lane's k run, its column's scale and zero.
+    const int col = wave * 32 + l32;  // output channel within the block
+    uint32_t a_lds[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a_lds[j] = (uint32_t)((l32 * 16 + ((8 * hh + j) ^ (l32 & 15))) * 16);
+    uint32_t b_lds[LANE_WORDS / 4];
+#pragma unroll
+    for (int v = 0; v < LANE_WORDS / 4; ++v)
+        b_lds[v] = (uint32_t)((col * CH + ((hh * (LANE_WORDS / 4) + v) ^ RB::swz(col))) * 16);
+    const uint32_t sz_lds = (uint32_t)(col * 16);
+    const uint32_t pair_mask = sgpr_const(F::kPairMask);
+    const uint32_t bias = vgpr_const(kBias2);
+
+    auto compute = [&](int step, auto sa_c, auto sb_c) {
+        constexpr int SA = decltype(sa_c)::value;
+        constexpr int SB = decltype(sb_c)::value;
+        const uint8_t* As = lds_a[SA];
+        const uint8_t* Bs = lds_b[SB];
+        const uint8_t* Sz = &lds_sz[(step >> 3) & 1][0][(step & 7) * 2];
+        const GroupConst gc = group_const(*(const uint16_t*)(Sz + sz_lds),
+                                          *(const uint16_t*)(Sz + 128 * 16 + sz_lds));
+        uint32_t wd[LANE_WORDS];
+#pragma unroll
+        for (int v = 0; v < LANE_WORDS / 4; ++v) {
+            const u32x4 t = *(const u32x4*)(Bs + b_lds[v]);
+            wd[4 * v + 0] = t[0];
+            wd[4 * v + 1] = t[1];
+            wd[4 * v + 2] = t[2];
+            wd[4 * v + 3] = t[3];
+        }
+        f16x8 a_cur[TM], a_nxt[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) a_cur[tm] = *(const f16x8*)(As + a_lds[0] + tm * 8192);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // the next slice's A reads are issued before this slice's MFMAs
+            // (the scheduler would otherwise sink each read next to its use)
+            if (j < 7) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    a_nxt[tm] = *(const f16x8*)(As + a_lds[j + 1] + tm * 8192);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // dequantise this slice's 8 codes: (1024 + q) pairs by one fused
+            // mask-and-or, then (q - z) exactly and one rounding of (q - z) s
+            const uint32_t w = wd[(8 * j) / F::kCodesPerWord];
+            const int p0 = ((8 * j) % F::kCodesPerWord) / 2;
+            f16x2 d[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t biased = ((w >> (BITS * (p0 + p))) & pair_mask) | bias;
+                d[p] = (as_f16x2(biased) + gc.nbz) * gc.s2;
+            }
+            const f16x8 b = f16x8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+                acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[tm], b, acc[tm], 0, 0, 0);
+            if (j < 7) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) a_cur[tm] = a_nxt[tm];
+            }
+        }
+    };
+
+    // DMA instructions this wave issued after its A DMAs of step g, by the end
+    // of iteration g - 1 (scale/zero DMAs not counted: waiting for fewer
+    // outstanding than exist is only stricter).
+    constexpr int C_STEADY = (RA - 2) * A_DMA + (RA - 1) * B_DMA;
+    static_assert(C_STEADY <= 63, "vmcnt field");
+    auto later_ops = [&](int g) {
+        const int na = min(g - 1, G - RA) - (g - RA + 2) + 1;
+        const int nb = min(g - 1, G - RBS) - (g - RA + 1) + 1;
+        return (na > 0 ? na : 0) * A_DMA + (nb > 0 ? nb : 0) * B_DMA;
+    };
+
+    for (int t = -(RBS - 1); t < 0; ++t) issue(t);
+    for (int g0 = 0; g0 < G; g0 += U) {
+        // steps g0 .. g0 + U - 1 with compile-time stage indices (g0 % U == 0)
+        for_each_index([&](auto u_c) {
+            constexpr int u = decltype(u_c)::value;
+            const int g = g0 + u;
+            if (g < G) {
+                wait_vmcnt_le<C_STEADY>(later_ops(g));
+                lds_barrier();
+                issue(g);
+                compute(g, std::integral_constant<int, u % RA>{},
+                        std::integral_constant<int, u % RBS>{});
+            }
+        }, std::make_integer_sequence<int, U>{});
+    }
+
+    const int n = n0 + col;
+    if (n >= N) return;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = m0 + 32 * tm + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (m >= M) continue;
+            if (part != nullptr) {
+                part[(int64_t)blockIdx.z * M * N + (int64_t)m * N + n] = acc[tm][r];
+            } else {
+                const uint16_t y = f32_to_f16_bits(acc[tm][r]);
+                Y[(int64_t)m * ldy + n] = y;
+                if (epi == kResidual) h[(int64_t)m * ldh + n] += (float)as_f16(y);
+            }
+        }
+    }
+}
+
 // Sum of the K-split partial tiles part[0..S)[M][N] in split order, rounded to
 // FP16, with the optional residual epilogue.  Four elements per thread.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
@@ -304,22 +662,33 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 struct Plan {
-    int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64
+    int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64, 3: ring 128x128
     int split;  // K parts
 };
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Tile choice, from a sweep on MI355X: with at least two 128x128 tiles per CU,
-// single-stage 128x128 workgroups (two resident per CU overlap each other's
-// barriers); with about one per CU, 128x128 on eight waves splitting each
-// step's k-slices in two; with fewer tiles, 64x64 workgroups of four 32x32
-// waves, several resident per CU.  When even that leaves CUs idle, K is split
-// over up to 8 parts of at least 4 groups (512 values) each.
-Plan plan_for(int M, int N, int K) {
+// Tile choice, from sweeps on MI355X over the block shapes and M = 32..2048.
+// The ring kernel (one workgroup per CU, operands prefetched by LDS DMA)
+// wins from about 192 128x128 tiles up to about 1024, and with K split into
+// parts of at least 8 groups when K >= 4096 gives too few tiles; it needs
+// aligned operands (ring = false otherwise).  Past 1024 tiles, single-stage
+// 128x128 workgroups (two resident per CU overlap each other's barriers);
+// with about one tile per CU, 128x128 on eight waves splitting each step's
+// k-slices in two; with fewer tiles, 64x64 workgroups of four 32x32 waves,
+// several resident per CU, K split over up to 8 parts of at least 4 groups.
+Plan plan_for(int M, int N, int K, bool ring) {
     const int groups = K / kBK;
     const int t128 = ceil_div(M, 128) * ceil_div(N, 128);
     const int t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    if (ring && groups % 8 == 0) {
+        if (t128 >= 192 && t128 < 1024) return {3, 1};
+        if (t128 < 192 && groups >= 32) {
+            int sp = 1;
+            while (sp < 8 && t128 * sp < 192) sp *= 2;
+            if (t128 * sp >= 192 && (groups / sp) % 8 == 0) return {3, sp};
+        }
+    }
     if (t128 >= 512) return {0, 1};
     if (t128 >= 240) return {1, 1};
     auto best_split = [&](int tiles) {
@@ -333,6 +702,15 @@ Plan plan_for(int M, int N, int K) {
     return {2, best_split(t64)};
 }
 
+// Second kernel of a K-split launch: the in-order reduction of the partials.
+hipError_t reduce_parts(const GemmArgs& a, int split, const float* part, hipStream_t s) {
+    const int64_t total = (int64_t)a.M * a.w->N;
+    const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
+    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, split, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
+                                           (int)a.epi);
+    return hipGetLastError();
+}
+
 template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int STAGES,
           int STORE_FROM>
 hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
@@ -344,20 +722,34 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
         a.ldh, (int)a.epi, a.w->K / kBK / split, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || split == 1) return e;
-    const int64_t total = (int64_t)a.M * a.w->N;
-    const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
-    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, split, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
-                                           (int)a.epi);
-    return hipGetLastError();
+    return reduce_parts(a, split, part, s);
+}
+
+template <int BITS, int BM, int RA, int RBS>
+hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
+    const int gx = (a.w->N + 127) / 128, gy = (a.M + BM - 1) / BM;
+    const double a_bytes = (double)BM * a.w->K * 2 / split;
+    const double b_bytes = 128.0 * a.w->K * BITS / 8 / split;
+    const Raster rs = make_raster(gx, gy, a_bytes, b_bytes);
+    dim3 grid(8 * rs.sx * rs.sy, 1, split);
+    float* part = split > 1 ? (float*)a.ws : nullptr;
+    k_gemm_ring<BITS, BM, RA, RBS><<<grid, 256, 0, s>>>(
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
+        a.ldh, (int)a.epi, a.w->K / kBK / split, part, rs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || split == 1) return e;
+    return reduce_parts(a, split, part, s);
 }
 
 template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
-    const Plan p = plan_for(a.M, a.w->N, a.w->K);
+    Plan p = plan_for(a.M, a.w->N, a.w->K, true);
+    if (p.cfg == 3 && !ring_ok(a, p.split)) p = plan_for(a.M, a.w->N, a.w->K, false);
     switch (p.cfg) {
         case 0: return launch_cfg<BITS, 128, 128, 2, 2, 1, 1, 0>(a, p.split, s);
         case 1: return launch_cfg<BITS, 128, 128, 2, 2, 2, 2, 2>(a, p.split, s);
-        default: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
+        case 2: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
+        default: return launch_ring<BITS, 128, 2, 4>(a, p.split, s);
     }
 }
 
@@ -367,9 +759,12 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t s) {
     return a.w->bits == 4 ? launch_bits<4>(a, s) : launch_bits<2>(a, s);
 }
 
+// Workspace for the K-split partials: enough for either plan, since whether
+// the ring kernel's alignment holds is known only at launch.
 size_t prefill_ws_bytes(int M, int N, int K) {
-    const Plan p = plan_for(M, N, K);
-    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    const Plan p = plan_for(M, N, K, true), q = plan_for(M, N, K, false);
+    const int split = p.split > q.split ? p.split : q.split;
+    return split > 1 ? (size_t)split * M * N * sizeof(float) : 0;
 }
 
 }  // namespace qg

@@ -86,6 +86,49 @@ def test_gemm_long_prefill_down_proj_sampled_rows(orc):
     assert np.all(np.isfinite(Y))
 
 
+# Shapes whose tile plan runs the LDS-DMA ring kernel: >= 192 output tiles of
+# 128 x 128 (ragged M and N edges), and K = 8192 with too few tiles, split
+# into 8 parts of 8 groups.  Rows are independent, so the oracle checks rows
+# at both edges of every 128-row block.
+RING_CASES = [(300, 2048, 8200), (130, 8192, 1500), (1024, 2048, 6144)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", RING_CASES)
+def test_gemm_ring_path_sampled_rows(orc, bits, M, K, N):
+    W, X = workloads.single_gemm(M, K, N, seed=M + K + N + bits)
+    p = qg.qg_pack(W.cuda(), bits)
+    op = orc.pack(W.numpy(), bits)
+    g = Guarded(M, N, (N + 15) // 8 * 8)
+    GEMM[bits](X.cuda(), p, Y=g.view)
+    torch.cuda.synchronize()
+    g.check()
+    Y = g.view.float().cpu().numpy()
+    rows = sorted({r for b in range(0, M, 128) for r in (b, min(b + 127, M - 1))} | {M - 1})
+    assert_close(Y[rows], orc.gemm(X.numpy()[rows], op), f"ring bits={bits} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_gemm_ring_shape_with_offset_scales(orc, offset):
+    """Scales and zeros as views starting `offset` halves into a larger
+    buffer: 16-byte aligned (offset 0) keeps the ring kernel, 2-byte aligned
+    (offset 1, which the format allows) must fall back to the staged kernel;
+    both match the oracle."""
+    M, K, N = 300, 2048, 8200
+    W, X = workloads.single_gemm(M, K, N, seed=offset)
+    p = qg.qg_pack(W.cuda(), 4)
+    op = orc.pack(W.numpy(), 4)
+    views = []
+    for t in (p.scales, p.zeros):
+        buf = torch.zeros(t.numel() + 8, dtype=torch.float16, device="cuda")
+        buf[offset:offset + t.numel()] = t.reshape(-1)
+        views.append(buf[offset:offset + t.numel()].view(t.shape))
+    shifted = qg.PackedWeight(4, K, N, p.codes, views[0], views[1])
+    Y = qg.qg_gemm_int4(X.cuda(), shifted).float().cpu().numpy()
+    rows = [0, 127, 128, 255, 256, 299]
+    assert_close(Y[rows], orc.gemm(X.numpy()[rows], op), f"offset={offset}")
+
+
 def _packed_from_codes(orc, bits, q, s, z):
     q = np.asarray(q, np.int64)
     N, K = q.shape
