@@ -183,6 +183,22 @@ def dequant(p: Packed) -> np.ndarray:
     return out
 
 
+def requant_4to2(p: Packed) -> Packed:
+    """INT4 -> INT2 re-quantisation ("β-Informed Deployment Features" page,
+    CTX-TIER, details of the shipped kernel: every group is dequantised, given
+    a new INT2 scale from its range, and packed four codes per byte).  Here:
+    the exact INT4 dequant w^ = (q - z) s, quantised again by `pack` with
+    bits = 2 under the same readings (range with 0 included, integer zero
+    point, round-half-even).  w^ has at most 15 significant bits, so its FP32
+    copy handed to `pack` is exact."""
+    if p.bits != 4:
+        raise OracleError("requant_4to2", EINVAL)
+    w = dequant(p)                                   # [N][K], FP64
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w), "INT4 dequant must be exact in FP32"
+    return pack(np.ascontiguousarray(w32.T), 2, p.group)
+
+
 def gemm(X, p: Packed) -> np.ndarray:
     """Y [M][N] = X [M][K] (FP16) @ w^ [K][N], FP64, unrounded."""
     X16 = np.ascontiguousarray(np.asarray(X, dtype=np.float16)).view(np.uint16)
