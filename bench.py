@@ -205,6 +205,29 @@ def extra_legs(qg, torch, workloads, args):
                                   "TFLOP/s": round(2.0 * 2048 * 8192 * 2048 / med / 1e12, 2),
                                   "frac_mfma": round(2.0 * 2048 * 8192 * 2048 / med / 1e12
                                                      / MFMA_F16_PEAK_TFLOPS, 4)}
+    del Xd, Y, p
+    sync()
+
+    # INT4 -> INT2 tier switch of the measured block: the four projections
+    # re-quantised out of place into preallocated INT2 weights.  Each call
+    # synchronises (it reports errors), so this is the caller-visible time;
+    # bytes = INT4 read + INT2 written (codes, scales and zeros).
+    inp = workloads.block(1, seed=0)
+    blk4 = qg.pack_block(inp.W, 4, D, F)
+    w4s = [blk4.qkv, blk4.out, blk4.up, blk4.down]
+    outs = [qg.PackedWeight.empty(w.K, w.N, 2, dev) for w in w4s]
+    for w, o in zip(w4s, outs):
+        qg.qg_requant_4to2(w, out=o)
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for w, o in zip(w4s, outs):
+            qg.qg_requant_4to2(w, out=o)
+    per = (time.perf_counter() - t0) / reps
+    moved = sum(w.nbytes() for w in w4s) + sum(o.nbytes() for o in outs)
+    out["next1_requant_int4_to_int2_block"] = {
+        "ms_per_block": round(per * 1e3, 4), "bytes_moved": moved,
+        "GB/s": round(moved / per / 1e9, 1), "frac_hbm": round(moved / per / 1e9 / HBM_PEAK_GBS, 4)}
     return out
 
 

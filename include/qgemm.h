@@ -100,6 +100,22 @@ const char* qg_last_error(void);
 int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int32_t group,
             uint32_t* codes, qg_half* scales, qg_half* zeros, void* stream);
 
+/* INT4 -> INT2 re-quantisation ("β-Informed Deployment Features" page,
+ * CTX-TIER, details of the shipped kernel: each group is dequantised and
+ * quantised again to INT2 with a new scale and zero).  Every group's exact
+ * INT4 dequant (q - z) s goes through qg_pack's quantiser with bits = 2; the
+ * result is bit-identical to that definition.
+ * w4: bits 4; w2: bits 2, same K and N; both described like any qg_weight
+ * (w2's codes are compact, [N][K/16]).  Out of place, w2's buffers must not
+ * overlap w4's or each other.  In place: w2->codes == w4->codes writes the
+ * INT2 codes compactly over the first half of the INT4 code buffer (the rest
+ * is left as it was), and w2->scales == w4->scales / w2->zeros == w4->zeros
+ * overwrite those arrays; any other overlap is QG_EINVAL.  Synchronises `stream` before returning (the caller may free
+ * or reuse the INT4 buffers at once), because it reports a non-finite INT4
+ * scale or zero, or an INT2 scale that overflows FP16, as QG_EINVAL (outputs
+ * are then unspecified). */
+int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream);
+
 /* Y[M][N] = X[M][K] . dequant(w)[K][N] (quant_gemm, "β-Informed Deployment
  * Features" page).  X FP16 [M][ldx], Y FP16 [M][ldy], ldx >= K, ldy >= N, both
  * multiples of 8 and 16-byte aligned pointers; FP32 accumulation, one
@@ -141,7 +157,7 @@ int qg_unpack(const qg_weight* w, uint8_t* q, void* stream);
 int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream);
 
 /* Frees library-owned device state (cached launch plans, the pack status
- * word) after synchronising the device.  Safe to call at any time when no
+ * word of qg_pack and qg_requant_4to2) after synchronising the device.  Safe to call at any time when no
  * library call is in flight on another thread. */
 void qg_release_cache(void);
 

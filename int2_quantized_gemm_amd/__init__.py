@@ -64,6 +64,7 @@ def _load():
                                               C.POINTER(sz), C.POINTER(sz)]),
         "qg_unpack": (C.c_int, [W, vp, vp]),
         "qg_dequant": (C.c_int, [W, i32, vp, vp]),
+        "qg_requant_4to2": (C.c_int, [W, W, vp]),
         "qg_release_cache": (None, []),
     }
     for name, (res, args) in sig.items():
@@ -257,6 +258,44 @@ def qg_dequant(w: PackedWeight, fp16: bool = False, stream=None) -> torch.Tensor
 
 def qg_release_cache() -> None:
     lib.qg_release_cache()
+
+
+def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place: bool = False,
+                    stream=None) -> PackedWeight:
+    """INT4 -> INT2 re-quantisation on the GPU; synchronises the stream.
+
+    Out of place the result goes to `out` (or new tensors).  With
+    in_place=True the INT2 codes are written compactly over the front of
+    w4.codes and the INT2 scales/zeros over w4's: the returned weight views
+    w4's memory, and w4 no longer holds INT4 data."""
+    if w4.bits != 4:
+        raise ValueError("w4 must be an INT4 weight")
+    K, N = w4.K, w4.N
+    if in_place:
+        if out is not None:
+            raise ValueError("in_place and out are exclusive")
+        if not w4.codes.is_contiguous():
+            raise ValueError("in place needs contiguous INT4 codes")
+        codes = w4.codes.view(-1)[:N * (K // 16)].view(N, K // 16)
+        out = PackedWeight(2, K, N, codes, w4.scales, w4.zeros)
+    elif out is None:
+        out = PackedWeight.empty(K, N, 2, w4.codes.device)
+    c4, c2 = w4.cstruct(), out.cstruct()
+    _check("qg_requant_4to2", lib.qg_requant_4to2(C.byref(c4), C.byref(c2), _stream(stream)))
+    return out
+
+
+def requant_block(blk: Block, in_place: bool = False, stream=None) -> Block:
+    """The INT4 -> INT2 tier switch of a loop block ("β-Informed Deployment
+    Features" page, CTX-TIER apply step): re-quantise each INT4 projection
+    (INT2 ones are kept).  Each call has synchronised the stream when it
+    returns, so the INT4 tensors may be dropped (out of place) as soon as the
+    caller releases `blk`."""
+    ws = {}
+    for k in ("qkv", "out", "up", "down"):
+        w = getattr(blk, k)
+        ws[k] = qg_requant_4to2(w, in_place=in_place, stream=stream) if w.bits == 4 else w
+    return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"])
 
 
 def pack_block(W: dict, bits: int, D: int, F: int, device="cuda") -> Block:

@@ -15,6 +15,8 @@ namespace qg {
 hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, uint32_t* codes,
                        qg_half* scales, qg_half* zeros, int* status, hipStream_t s);
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s);
+hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
+                               int* status, hipStream_t s);
 hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s);
 
 // ---- GEMM (kernels_gemm.hip)

@@ -1,0 +1,144 @@
+// kernels_requant.hip -- INT4 -> INT2 re-quantisation on the device
+// (qg_requant_4to2).
+//
+// "β-Informed Deployment Features" page, CTX-TIER, details of the shipped
+// kernel: each quantisation group is dequantised, given a new asymmetric INT2
+// scale from its range and packed four codes per byte, in place or into a
+// separate buffer.  Here each group's exact INT4 dequant w^ = (q - z) s (FP64)
+// goes through the same quantiser as qg_pack with bits = 2: range with 0
+// included, s2 = fp16((hi - lo) / 3) (1 when it rounds to 0), integer zero
+// z2 = rne(-lo / s2), codes rne(w^ / s2) + z2, all clamped to [0, 3], FP64
+// with correctly rounded division -- bit-identical to the definition.
+//
+// Four lanes per group: lane r takes INT4 words 4r .. 4r+3 of the group (32
+// codes).  The group's range needs only its smallest and largest INT4 code
+// (w^ is monotone in q): lo = min(0, (qmin - z) s, (qmax - z) s), likewise hi.
+// The INT2 code of a weight depends only on its INT4 code (0..15), so lane r
+// computes the INT2 codes of INT4 values 4r .. 4r+3 with the definition's
+// FP64 steps, the four lanes OR them into one 32-bit table of sixteen 2-bit
+// codes, and every weight's code is a shift and mask of that table.  Lane r
+// then writes INT2 words 2r, 2r+1 of the group.  A wave covers 16 groups; its
+// reads and writes are contiguous.
+// In place the INT2 codes are written compactly (K/16 words per row) over the
+// front of the INT4 buffer: INT2 group (n, g) lands inside INT4 group
+// (n/2, ...) of the same buffer, so it may be written only once that INT4
+// data has been read.  Row 0 runs group ranges [0, 1), [1, 2), [2, 4), ...
+// (group g writes into INT4 group g/2 of row 0, consumed by an earlier launch;
+// group 0 writes into itself, which is safe within its one wave because every
+// lane's load feeds the shuffled OR before any lane stores), then rows
+// [1, 2), [2, 4), [4, 8), ... (INT2 row n lies in INT4 row n/2, consumed by
+// an earlier launch; none of the rows a launch reads has been written).  The
+// pages' in-place mode keeps the INT4 row stride instead; the weight
+// descriptor here has no row stride, so the compact form is the one the INT2
+// GEMM can read.  Scales and zeros are overwritten element for element by
+// the lane that read them.
+#include "device.h"
+#include "internal.h"
+
+namespace qg {
+namespace {
+
+__global__ __launch_bounds__(256) void k_requant_4to2(
+    const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
+    int g0, int gcount, uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status) {
+    const int groups = K / kGroup;
+    // grid: x over the groups of a row (4 lanes each), y over the rows
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int r = t & 3;
+    const bool live = (t >> 2) < gcount;  // all 4 lanes of a group alike
+    const int64_t n = row0 + blockIdx.y;
+    const int g = g0 + (live ? (t >> 2) : 0);
+    const int64_t sg = n * groups + g;
+
+    u32x4 w4 = {0u, 0u, 0u, 0u};
+    double s4 = 0.0, z4 = 0.0;
+    if (live) {
+        w4 = *(const u32x4*)(codes4 + n * (K / 8) + g * 16 + 4 * r);
+        s4 = f16_bits_to_f64(scales4[sg]);
+        z4 = f16_bits_to_f64(zeros4[sg]);
+    }
+    // smallest and largest INT4 code of the group
+    int qmin = 15, qmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int q = (int)((w4[i] >> (16 * (j & 1) + 4 * (j >> 1))) & 0xFu);
+            qmin = q < qmin ? q : qmin;
+            qmax = q > qmax ? q : qmax;
+        }
+#pragma unroll
+    for (int m = 2; m >= 1; m >>= 1) {
+        const int a = __shfl_xor(qmin, m, 4), b = __shfl_xor(qmax, m, 4);
+        qmin = a < qmin ? a : qmin;
+        qmax = b > qmax ? b : qmax;
+    }
+    const double wa = ((double)qmin - z4) * s4, wb = ((double)qmax - z4) * s4;
+    const double lo = fmin(0.0, fmin(wa, wb)), hi = fmax(0.0, fmax(wa, wb));
+    uint16_t s_store = f64_to_f16_bits((hi - lo) / 3.0);
+    double s2 = f16_bits_to_f64(s_store);
+    const bool bad = live && (!isfinite(s4) || !isfinite(z4) || !isfinite(s2));
+    if (s2 == 0.0) {
+        s2 = 1.0;
+        s_store = 0x3c00;  // 1.0
+    }
+    double z2 = rint(-lo / s2);
+    z2 = z2 < 0.0 ? 0.0 : (z2 > 3.0 ? 3.0 : z2);
+    // INT2 codes of INT4 values 4r .. 4r+3, then the whole 16-entry table
+    uint32_t table = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        double q = rint((((double)(4 * r + v) - z4) * s4) / s2) + z2;
+        q = q >= 0.0 ? q : 0.0;  // also maps NaN to 0 (reported via status)
+        q = q > 3.0 ? 3.0 : q;
+        table |= (uint32_t)q << (2 * (4 * r + v));
+    }
+    table |= (uint32_t)__shfl_xor((int)table, 1, 4);
+    table |= (uint32_t)__shfl_xor((int)table, 2, 4);
+    if (!live) return;
+    // INT4 words 4r + 2i, 4r + 2i + 1 hold the 16 codes of INT2 word 2r + i
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t q4 = (w4[i] >> (16 * (j & 1) + 4 * (j >> 1))) & 0xFu;
+            const uint32_t q2 = (table >> (2 * q4)) & 3u;
+            const int jj = 8 * (i & 1) + j;  // code index inside the INT2 word
+            out[i >> 1] |= q2 << (16 * (jj & 1) + 2 * (jj >> 1));
+        }
+    *(u32x2*)(codes2 + n * (K / 16) + g * 8 + 2 * r) = u32x2{out[0], out[1]};
+    if (r == 0) {
+        scales2[sg] = s_store;
+        zeros2[sg] = f64_to_f16_bits(z2);
+    }
+    if (bad) atomicOr(status, 1);
+}
+
+}  // namespace
+
+hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
+                               int* status, hipStream_t s) {
+    const int K = w4.K, N = w4.N, groups = K / kGroup;
+    uint32_t* c2 = const_cast<uint32_t*>(w2.codes);
+    uint16_t* s2 = const_cast<uint16_t*>(w2.scales);
+    uint16_t* z2 = const_cast<uint16_t*>(w2.zeros);
+    auto run = [&](int row0, int rows, int g0, int gcount) {
+        // workgroups of one to four waves, as many as a row's groups fill
+        const int lanes = gcount * 4;
+        const int threads = lanes >= 256 ? 256 : (lanes + 63) / 64 * 64;
+        const dim3 grid((unsigned)((lanes + threads - 1) / threads), (unsigned)rows);
+        k_requant_4to2<<<grid, threads, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, row0, g0,
+                                                gcount, c2, s2, z2, status);
+        return hipGetLastError();
+    };
+    if (!in_place) return run(0, N, 0, groups);
+    hipError_t e = run(0, 1, 0, 1);
+    for (int lo = 1; e == hipSuccess && lo < groups; lo *= 2)
+        e = run(0, 1, lo, (2 * lo < groups ? 2 * lo : groups) - lo);
+    for (int64_t lo = 1; e == hipSuccess && lo < N; lo *= 2)
+        e = run((int)lo, (int)((2 * lo < N ? 2 * lo : N) - lo), 0, groups);
+    return e;
+}
+
+}  // namespace qg

@@ -267,7 +267,8 @@ hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, v
     return hipSuccess;
 }
 
-// Per-device status word for qg_pack (library-owned, freed by qg_release_cache).
+// Per-device status word for qg_pack and qg_requant_4to2 (library-owned, freed by
+// qg_release_cache).
 std::mutex g_pack_mu;
 int* g_pack_status[64] = {nullptr};
 
@@ -319,6 +320,76 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     if (host)
         return fail(QG_EINVAL, "%s: W holds a non-finite value or a group whose scale overflows "
                                "FP16", fn);
+    return ok();
+}
+
+// [p, p + bytes) and [q, q + bytes2) share a byte.
+static bool overlaps(const void* p, size_t bytes, const void* q, size_t bytes2) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + bytes2 && b < a + bytes;
+}
+
+int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
+    const char* fn = "qg_requant_4to2";
+    if (!w4 || !w2) return fail(QG_EINVAL, "%s: w4 and w2 must be non-NULL", fn);
+    int st = check_weight(w4, fn, "w4");
+    if (st) return st;
+    st = check_weight(w2, fn, "w2");
+    if (st) return st;
+    if (w4->bits != 4 || w2->bits != 2)
+        return fail(QG_EINVAL, "%s: w4.bits = %d and w2.bits = %d must be 4 and 2", fn, w4->bits,
+                    w2->bits);
+    if (w2->K != w4->K || w2->N != w4->N)
+        return fail(QG_EINVAL, "%s: w2 is %d x %d but w4 is %d x %d (K x N)", fn, w2->K, w2->N,
+                    w4->K, w4->N);
+    const int groups = w4->K / 128;
+    const size_t c4 = (size_t)w4->N * (w4->K / 8) * 4, c2 = (size_t)w4->N * (w4->K / 16) * 4;
+    const size_t sz = (size_t)w4->N * groups * 2;
+    const void* in[3] = {w4->codes, w4->scales, w4->zeros};
+    const size_t in_bytes[3] = {c4, sz, sz};
+    const void* out[3] = {w2->codes, w2->scales, w2->zeros};
+    const size_t out_bytes[3] = {c2, sz, sz};
+    // each output is either its own input (in place) or apart from every
+    // input, and the outputs are apart from each other
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j) {
+            if (i == j && out[i] == in[j]) continue;
+            if (overlaps(out[i], out_bytes[i], in[j], in_bytes[j]))
+                return fail(QG_EINVAL, "%s: output %s overlaps input %s (only exact in-place "
+                                       "aliasing of codes, scales or zeros is allowed)", fn,
+                            i == 0 ? "codes" : i == 1 ? "scales" : "zeros",
+                            j == 0 ? "codes" : j == 1 ? "scales" : "zeros");
+        }
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j]))
+                return fail(QG_EINVAL, "%s: the outputs overlap each other", fn);
+    }
+    const bool in_place = w2->codes == w4->codes;
+    hipStream_t s = (hipStream_t)stream;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    if (!g_pack_status[dev]) {
+        e = hipMalloc((void**)&g_pack_status[dev], sizeof(int));
+        if (e != hipSuccess) {
+            g_pack_status[dev] = nullptr;
+            return fail(QG_ENOMEM, "%s: cannot allocate the 4-byte status word (%s)", fn,
+                        hipGetErrorString(e));
+        }
+    }
+    int* stw = g_pack_status[dev];
+    if ((e = hipMemsetAsync(stw, 0, sizeof(int), s)) != hipSuccess) return hip_fail(fn, e);
+    if ((e = qg::launch_requant_4to2(*w4, *w2, in_place, stw, s)) != hipSuccess)
+        return hip_fail(fn, e);
+    int host = 0;
+    if ((e = hipMemcpyAsync(&host, stw, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return hip_fail(fn, e);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(fn, e);
+    if (host)
+        return fail(QG_EINVAL, "%s: w4 holds a non-finite scale or zero, or a group whose INT2 "
+                               "scale overflows FP16", fn);
     return ok();
 }
 

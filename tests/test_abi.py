@@ -144,3 +144,29 @@ def test_product_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
                 assert "from oracle" not in text, f
+
+
+def _rq(w4, w2):
+    return qg.lib.qg_requant_4to2(C.byref(w4), C.byref(w2), None)
+
+
+# INT4 2048 x 2048: codes 2 MiB, scales/zeros 32 KiB each; INT2 codes 1 MiB.
+_C4, _S4, _Z4 = FAKE, FAKE + (4 << 20), FAKE + (5 << 20)
+_C2, _S2, _Z2 = FAKE + (8 << 20), FAKE + (12 << 20), FAKE + (13 << 20)
+
+
+@pytest.mark.parametrize("w4kw,w2kw,needle", [
+    (dict(bits=2), dict(bits=2), "bits"),
+    (dict(), dict(bits=4), "bits"),
+    (dict(), dict(K=4096), "K x N"),
+    (dict(), dict(N=1024), "K x N"),
+    (dict(), dict(codes=_C4 + 64), "overlaps input codes"),      # partial overlap
+    (dict(), dict(scales=_C4), "overlaps input codes"),
+    (dict(), dict(zeros=_S4 + 2), "overlaps input scales"),
+    (dict(), dict(codes=_S2), "outputs overlap"),
+])
+def test_requant_rejects_bad_arguments(w4kw, w2kw, needle):
+    w4 = _w(**{**dict(bits=4, codes=_C4, scales=_S4, zeros=_Z4), **w4kw})
+    w2 = _w(**{**dict(bits=2, codes=_C2, scales=_S2, zeros=_Z2), **w2kw})
+    assert _rq(w4, w2) == qg.QG_EINVAL
+    assert needle in qg.qg_last_error()
