@@ -93,12 +93,96 @@ def traffic_record(kernel_key: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "int2_quantized_gemm_amd", "csrc", "kernels_gemm.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256(open(os.path.join(ROOT, GEMV_SRC), "rb").read()).hexdigest()[:16]
     e = rec.get(kernel_key)
     if not e or e.get("source_sha256_16") != h:
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 256 << 20  # calibration copy: larger than the 256 MB MALL's share it can hold
+GEMV_KEY = "gemv_int4_k8192_n2048"
+GEMV_SRC = os.path.join("int2_quantized_gemm_amd", "csrc", "kernels_gemm.hip")
+
+
+def pmc_target(qg, torch, workloads, launches: int = 50):
+    """Counter target: the roofline kernel (down-projection GEMV, same weights
+    and grid as the roofline leg) launched eagerly `launches` times after a
+    warm-up, then `launches` device-to-device copies of COPY_BYTES, the
+    calibration kernel of known traffic."""
+    dev = "cuda"
+    inp = workloads.block(1, seed=0)
+    down = qg.qg_pack(inp.W["down"].to(dev), 4)
+    u = torch.empty(1, F, dtype=torch.float16, device=dev).normal_()
+    y = torch.empty(1, D, dtype=torch.float16, device=dev)
+    for _ in range(5):
+        qg.qg_gemm_int4(u, down, Y=y)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        qg.qg_gemm_int4(u, down, Y=y)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"pmc target: {launches} GEMV launches ({down.nbytes()} algorithmic bytes each), "
+        f"{launches} copies of {COPY_BYTES} bytes")
+
+
+def traffic_from(fetch_csv: str, write_csv: str, command: str):
+    """HBM bytes per launch of the roofline GEMV from two rocprofv3 --pmc runs
+    of --pmc-target (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by expected / counted bytes of the calibration copy; written to
+    profiles/traffic.json under the kernel source's hash."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter):
+        tot = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            k = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            tot[k] = tot.get(k, 0.0) + float(row["Counter_Value"])
+        gemv = [v for (d, n), v in sorted(tot.items()) if "k_gemv" in n]
+        copy = [v for (d, n), v in sorted(tot.items()) if "copy" in n.lower()]
+        big = max(copy)
+        # drop the GEMV warm-up launches and the small host-side copies
+        return gemv[5:], [v for v in copy if v > 0.25 * big]
+
+    g_f, c_f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    g_w, c_w = per_dispatch(write_csv, "WRITE_SIZE")
+    med = statistics.median
+    kib = 1024.0
+    scale_f = COPY_BYTES / (med(c_f) * kib)
+    scale_w = COPY_BYTES / (med(c_w) * kib)
+    fetch_b = med(g_f) * kib * scale_f
+    write_b = med(g_w) * kib * scale_w
+    src = os.path.join(ROOT, GEMV_SRC)
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(rec_path)) if os.path.exists(rec_path) else {}
+    rec[GEMV_KEY] = {
+        "kernel": "k_gemv<4,64,4,2,false> (K=8192, N=2048, M=1)",
+        "source": GEMV_SRC,
+        "source_sha256_16": hashlib.sha256(open(src, "rb").read()).hexdigest()[:16],
+        "fetch_kib_per_launch_raw": round(med(g_f), 1),
+        "write_kib_per_launch_raw": round(med(g_w), 1),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib_raw": round(med(c_f), 1),
+        "copy_write_kib_raw": round(med(c_w), 1),
+        "scale_fetch": round(scale_f, 4),
+        "scale_write": round(scale_w, 4),
+        "fetch_bytes_per_launch": int(fetch_b),
+        "write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+        "launches": [len(g_f), len(g_w)],
+        "command": command,
+    }
+    with open(rec_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec[GEMV_KEY]))
 
 
 def cpu_baseline(budget_s: float):
@@ -239,7 +323,18 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-target", action="store_true",
+                    help="only launch the roofline kernel and the calibration copy (for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the two counter runs (no GPU)")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command lines that produced the counter runs, recorded as is")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.traffic_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path "
@@ -254,6 +349,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.pmc_target:
+        pmc_target(qg, torch, workloads)
+        return
 
     # ---- main leg: INT4 loop block, M=1, L=8 (decode)
     inp = workloads.block(1, seed=0)
@@ -273,7 +371,7 @@ def main():
     avg_s = graph_leg(torch, lambda i: qg.qg_gemm_int4(u, blk.down, Y=y), 200, replays=5)
     down_bytes = blk.down.nbytes()
     achieved = down_bytes / avg_s / 1e9
-    traffic = traffic_record("gemv_int4_k8192_n2048")
+    traffic = traffic_record(GEMV_KEY)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
