@@ -37,10 +37,12 @@ struct GemmArgs {
     int64_t ldh;
     void* ws;
     size_t ws_bytes;
-    // M == 1 GEMV only: when ln_h is set, the activations are fp16(LN(ln_h))
-    // (ln_h FP32 [K]) and X is ignored; norm_out, if set, receives them.
+    // M == 1 GEMV only (where gemm_fuses_layernorm holds): when ln_h is set,
+    // the activations are fp16(LN(ln_h)) (ln_h FP32 [K]) and X is ignored;
+    // norm_out, if set, receives them.
     const float* ln_h = nullptr;
     qg_half* norm_out = nullptr;
+
 };
 
 // True when a GEMM of this shape can take its activations as the fused
@@ -55,6 +57,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // M > 16: LDS-staged, double-buffered MFMA GEMM (kernels_prefill.hip); when it
 // splits K, a.ws must hold prefill_ws_bytes(M, N, K) bytes of FP32 partials.
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t s);
+// Deterministic sum of K-split partials part[0..S)[M][N] (FP32, in split
+// order) into a.Y with a's epilogue.
+hipError_t launch_splitk_reduce(const float* part, int S, const GemmArgs& a, hipStream_t s);
 size_t prefill_ws_bytes(int M, int N, int K);
 
 // ---- loop glue (kernels_loop.hip)

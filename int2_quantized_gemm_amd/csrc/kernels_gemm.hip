@@ -307,67 +307,98 @@ __device__ __forceinline__ void store_out(uint16_t* Y, int64_t ldy, float* h, in
 
 // ---------------------------------------------------------------- skinny ----
 
-// 16 output channels per workgroup, K split over KSPLIT waves, each wave
-// owning at most GPW groups.  All loads of a wave (codes, scales, zeros and
-// the 16 activation rows of its k range) are issued before its first MFMA,
-// so the wave pays one memory latency.  Rows past N or M are clamped for the
-// loads and zeroed by value (scale 0, activation 0): no branches around loads.
-// The KSPLIT partial tiles are summed through LDS in wave order.
-template <int BITS, int KSPLIT, int GPW>
-__global__ __launch_bounds__(64 * KSPLIT) void k_gemm_skinny(
+// 2 <= M <= 16.  A workgroup of four waves computes 16 output channels over
+// one K part (at most kSkinnyMaxK values; K is cut into S parts, summed by
+// k_splitk_reduce when S > 1).  The activation rows of the part are staged
+// once in LDS -- 16 rows (rows past M are zero or unused) of R values,
+// 16-byte chunk ci of row m at chunk slot ci ^ (m % 16), so the fragment
+// reads of the 16 rows hit distinct banks -- by LDS DMA of contiguous row
+// pieces; the MFMA A fragments then come from LDS instead of 16-byte pieces of
+// 16 rows 2K bytes apart in global memory, which had kept the skinny shapes
+// far from the GEMV's bandwidth (measured: 15 us -> 8 us plus the reduction
+// for M = 16, K = 8192, N = 2048).  Wave w takes the part's groups w, w+4, ...;
+// the four partial tiles are summed through LDS in wave order.  (Normalising
+// h inside this kernel, as the GEMV does, costs more than the LayerNorm
+// kernel: every workgroup must read all M rows of h.)
+constexpr int kSkinnyMaxK = 2048;
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi) {
-    using F = Fmt<BITS>;
-    __shared__ f32x4 red[KSPLIT][64];
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N, int S,
+    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
+    float* __restrict__ part) {
+    constexpr int kMaxGpw = kSkinnyMaxK / kGroup / 4;  // groups per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[16 * kSkinnyMaxK * 2];
+    __shared__ f32x4 red[4][64];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, c = lane >> 4;
     const int n = blockIdx.x * 16 + nl;
     const bool nvalid = n < N;
-    const bool mvalid = nl < M;
     const int groups = K / kGroup;
-    const int g0 = (int)((int64_t)groups * wave / KSPLIT);
-    const int gn = (int)((int64_t)groups * (wave + 1) / KSPLIT) - g0;  // <= GPW
+    const int p = blockIdx.y;
+    const int gbeg = (int)((int64_t)groups * p / S);
+    const int gcnt = (int)((int64_t)groups * (p + 1) / S) - gbeg;  // <= kSkinnyMaxK / 128
+    const int cpr = gcnt * 16;  // 16-byte chunks per staged row
     const int nr = nvalid ? n : N - 1;
-    const uint32_t* crow = codes + (int64_t)nr * (K / F::kCodesPerWord);
-    const uint16_t* xrow = X + (int64_t)(mvalid ? nl : M - 1) * ldx;
+    const uint32_t* crow = codes + (int64_t)nr * (K / Fmt<BITS>::kCodesPerWord);
 
-    LaneCodes<BITS> lc[GPW];
-    uint16_t sb[GPW], zb[GPW];
-    f16x8 a[GPW][4];
+    // weights of this wave's groups first (rows past N clamped, zeroed by scale)
+    LaneCodes<BITS> lc[kMaxGpw];
+    uint16_t sb[kMaxGpw], zb[kMaxGpw];
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        const int g = g0 + (i < gn ? i : 0);  // spare slots reload group g0 (unused)
-        lc[i].load(crow, g, c);
-        sb[i] = scales[(int64_t)nr * groups + g];
-        zb[i] = zeros[(int64_t)nr * groups + g];
-        const f16x8* p = (const f16x8*)(xrow + g * kGroup + c * 32);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[i][j] = p[j];
+    for (int i = 0; i < kMaxGpw; ++i) {
+        const int gi = wave + 4 * i;
+        if (gi < gcnt) {
+            const int g = gbeg + gi;
+            lc[i].load(crow, g, c);
+            sb[i] = nvalid ? scales[(int64_t)nr * groups + g] : (uint16_t)0;
+            zb[i] = zeros[(int64_t)nr * groups + g];
+        }
     }
-    const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    // the part's activation rows, 1 KiB per DMA instruction
+    const i32x4 rx = make_rsrc_sgpr(X, ((int64_t)(M - 1) * ldx + K) * 2);
+    const int units = 16 * cpr;
+    for (int u0 = wave * 64; u0 < units; u0 += 256) {
+        const int u = u0 + lane;
+        const int row = u / cpr, slot = u % cpr;
+        const int ci = slot ^ (row & 15);
+        dma16(rx, xs + u0 * 16, (uint32_t)((row * ldx + (int64_t)gbeg * kGroup + ci * 8) * 2));
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = zero4;
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        if (i < gn) {
-            const GroupConst gc = group_const(nvalid ? sb[i] : (uint16_t)0, zb[i]);
+    for (int i = 0; i < kMaxGpw; ++i) {
+        const int gi = wave + 4 * i;
+        if (gi < gcnt) {
+            const GroupConst gc = group_const(sb[i], zb[i]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc = mfma16(mvalid ? a[i][j] : zero8, lc[i].frag(j, gc), acc);
+            for (int j = 0; j < 4; ++j) {
+                const int ci = gi * 16 + 4 * c + j;  // row nl, k = 128 gi + 32 c + 8 j
+                const f16x8 a = *(const f16x8*)(xs + (nl * cpr + (ci ^ nl)) * 16);
+                acc = mfma16(a, lc[i].frag(j, gc), acc);
+            }
         }
     }
     red[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0 || !nvalid) return;
     f32x4 sum = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < KSPLIT; ++w) sum += red[w][lane];
-    if (!nvalid) return;
+    for (int w = 1; w < 4; ++w) sum += red[w][lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * c + r;
-        if (m < M) store_out(Y, ldy, h, ldh, epi, m, n, sum[r]);
+        if (m >= M) continue;
+        if (part != nullptr)
+            part[(int64_t)p * M * N + (int64_t)m * N + n] = sum[r];
+        else
+            store_out(Y, ldy, h, ldh, epi, m, n, sum[r]);
     }
 }
 
@@ -459,24 +490,20 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
 
 // K split so that each wave owns at most 4 groups: 4 waves up to K = 2048,
 // 8 up to 4096, 16 up to 8192.
+// K parts of the skinny kernel: enough that each spans at most kSkinnyMaxK.
+int skinny_parts(int K) { return (K + kSkinnyMaxK - 1) / kSkinnyMaxK; }
+
 template <int BITS>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-    const int groups = a.w->K / kGroup;
-    const int blocks = (a.w->N + 15) / 16;
-#define QG_SKINNY(KS, GPW)                                                                      \
-    k_gemm_skinny<BITS, KS, GPW><<<blocks, 64 * KS, 0, s>>>(                                    \
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h, \
-        a.ldh, (int)a.epi)
-    if (groups <= 16)
-        QG_SKINNY(4, 4);
-    else if (groups <= 32)
-        QG_SKINNY(8, 4);
-    else if (groups <= 64)
-        QG_SKINNY(16, 4);
-    else
-        return hipErrorInvalidValue;  // not dispatched: gemm_path sends K > 8192 to the tiled path
-#undef QG_SKINNY
-    return hipGetLastError();
+    const int S = skinny_parts(a.w->K);
+    const dim3 grid((a.w->N + 15) / 16, S);
+    float* part = S > 1 ? (float*)a.ws : nullptr;
+    k_gemm_skinny<BITS><<<grid, 256, 0, s>>>(a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros,
+                                             a.w->K, a.w->N, S, a.Y, a.ldy, a.h, a.ldh,
+                                             (int)a.epi, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    return launch_splitk_reduce(part, S, a, s);
 }
 
 }  // namespace
@@ -484,7 +511,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 GemmPath gemm_path(int bits, int M, int K, int N) {
     (void)N;
     if (M == 1 && gemv_shape(bits, K).ok) return kPathGemv;
-    if (M <= 16 && K <= 8192) return kPathSkinny;
+    if (M <= 16 && K <= 4 * kSkinnyMaxK) return kPathSkinny;
     return kPathTiled;
 }
 
@@ -493,7 +520,14 @@ bool gemm_fuses_layernorm(int bits, int M, int K, int N) {
 }
 
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {
-    return gemm_path(bits, M, K, N) == kPathTiled ? prefill_ws_bytes(M, N, K) : 0;
+    switch (gemm_path(bits, M, K, N)) {
+        case kPathSkinny: {
+            const int S = skinny_parts(K);
+            return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+        }
+        case kPathTiled: return prefill_ws_bytes(M, N, K);
+        default: return 0;
+    }
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

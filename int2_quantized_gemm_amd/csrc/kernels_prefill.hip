@@ -282,60 +282,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     }
 }
 
-// Buffer descriptor as four SGPRs (base, no stride, num_records bytes, raw
-// buffer flags as for make_rsrc), for the inline-asm LDS DMA below.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 make_rsrc_sgpr(const void* base, int64_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    const int32_t n = bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)(bytes < 0 ? 0 : bytes);
-    return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
-                 __builtin_amdgcn_readfirstlane((int32_t)((b >> 32) & 0xFFFF)),
-                 __builtin_amdgcn_readfirstlane(n), 0x00020000};
-}
-
-// One 16-byte-per-lane buffer load written straight to LDS (lane l's bytes
-// land at lds + 16 l; the wave's LDS base goes through M0, which an LDS DMA
-// may read only one wait state after the SALU write).  Issued as inline
-// asm so that the compiler does not wait for it before unrelated LDS reads:
-// completion is the caller's business (wait_vmcnt, then a barrier).  Out of
-// range offsets read as zero.
-__device__ __forceinline__ void dma16(i32x4 rsrc, const void* lds, uint32_t voffset) {
-    const int32_t m0 = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are pending
-// (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt not waited).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// Workgroup barrier for LDS producers/consumers whose vector-memory waits are
-// explicit: finishes this wave's LDS accesses, then s_barrier.  The asm
-// memory clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most c (runtime, 0 <= c) vector-memory operations are
-// pending; c >= N is treated as N.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le(int c) {
-    if constexpr (N == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (c >= N)
-            wait_vmcnt<N>();
-        else
-            wait_vmcnt_le<N - 1>(c);
-    }
-}
-
 // 32-bit constants in registers the compiler cannot fold (an SGPR and a
 // VGPR), so that a mask and an OR constant meet in one fused VOP3 instruction
 // (v_and_or / v_bitop3), which can take neither a literal nor two SGPRs.
@@ -702,13 +648,8 @@ Plan plan_for(int M, int N, int K, bool ring) {
     return {2, best_split(t64)};
 }
 
-// Second kernel of a K-split launch: the in-order reduction of the partials.
 hipError_t reduce_parts(const GemmArgs& a, int split, const float* part, hipStream_t s) {
-    const int64_t total = (int64_t)a.M * a.w->N;
-    const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
-    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, split, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
-                                           (int)a.epi);
-    return hipGetLastError();
+    return launch_splitk_reduce(part, split, a, s);
 }
 
 template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int STAGES,
@@ -754,6 +695,16 @@ hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Second kernel of a K-split launch: the in-order reduction of the partials
+// part[0..S)[M][N] into Y (and h for the residual epilogue).
+hipError_t launch_splitk_reduce(const float* part, int S, const GemmArgs& a, hipStream_t s) {
+    const int64_t total = (int64_t)a.M * a.w->N;
+    const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
+    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, S, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
+                                           (int)a.epi);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t s) {
     return a.w->bits == 4 ? launch_bits<4>(a, s) : launch_bits<2>(a, s);

@@ -94,6 +94,16 @@ RING_CASES = [(300, 2048, 8200), (130, 8192, 1500), (1024, 2048, 6144)]
 
 
 @pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", [(2, 6144, 40), (16, 8192, 2048), (5, 2304, 104),
+                                   (16, 2048, 8192), (11, 4096, 200)])
+def test_gemm_skinny_k_parts(orc, bits, M, K, N):
+    """2 <= M <= 16 with K above the staging size: K split into parts and
+    summed by the reduction kernel (uneven parts for K = 2304 and 6144)."""
+    Y, ref = _case(orc, bits, M, K, N, seed=M + K + N, ld_pad=8, ldx_pad=8)
+    assert_close(Y, ref, f"skinny parts bits={bits} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("M,K,N", RING_CASES)
 def test_gemm_ring_path_sampled_rows(orc, bits, M, K, N):
     W, X = workloads.single_gemm(M, K, N, seed=M + K + N + bits)

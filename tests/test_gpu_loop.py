@@ -49,6 +49,26 @@ def test_loop_small_block_full(orc, bits, M):
     _check_scratch(qg.scratch_views(blk, M, scratch), last, slice(None), f"bits={bits} M={M}")
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [2, 9, 16])
+def test_loop_skinny_k_parts(orc, bits, M):
+    """2 <= M <= 16 through the whole block with F = 4608: the down projection
+    runs as three K parts and the split reduction with the residual epilogue."""
+    D, F, L = 512, 4608, 2
+    inp, blk, oblk = _blocks(orc, M, bits, D, F, seed=40 + M)
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    href, last = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
+    _check_h(h.cpu().numpy(), href, f"h bits={bits} M={M}")
+    _check_scratch(qg.scratch_views(blk, M, scratch), last, slice(None), f"bits={bits} M={M}")
+    # one iteration per call gives the same bits
+    split = inp.X.float().cuda()
+    for l in range(L):
+        qg.qg_loop_range(blk, split, l, l + 1, scratch)
+    assert torch.equal(split, h)
+
+
 @pytest.mark.parametrize("M", [1, 16, 40])
 def test_loop_empty_range_split_and_repeat(orc, M):
     D, F = 256, 512
