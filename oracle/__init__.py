@@ -46,7 +46,8 @@ class _Weight(C.Structure):
 
 class _Block(C.Structure):
     _fields_ = [("D", C.c_int32), ("F", C.c_int32),
-                ("qkv", _Weight), ("out", _Weight), ("up", _Weight), ("down", _Weight)]
+                ("qkv", _Weight), ("out", _Weight), ("up", _Weight), ("down", _Weight),
+                ("gate", _Weight)]
 
 
 def lib():
@@ -73,7 +74,9 @@ def lib():
         L.or_layernorm.restype = C.c_int
         L.or_layernorm.argtypes = [vp, i32, i32, vp]
         L.or_loop_range.restype = C.c_int
-        L.or_loop_range.argtypes = [C.POINTER(_Block), vp, i32, i32, i32, vp, vp, vp, vp]
+        L.or_loop_range.argtypes = [C.POINTER(_Block), vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.or_silu.restype = C.c_double
+        L.or_silu.argtypes = [C.c_double]
         for name in ("or_round_half_array", "or_half_to_double_array"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [vp, i64, vp]
@@ -219,31 +222,48 @@ def layernorm(h) -> np.ndarray:
 
 @dataclass
 class Block:
+    """The block's projections; gate None = four projections with the
+    identity FFN activation, else the SwiGLU FFN (see or_block in oracle.c)."""
     D: int
     F: int
     qkv: Packed
     out: Packed
     up: Packed
     down: Packed
+    gate: Packed | None = None
 
     def cstruct(self) -> _Block:
+        gate = self.gate.cstruct() if self.gate is not None else _Weight(0, 0, 0, 0, None, None,
+                                                                           None)
         return _Block(self.D, self.F, self.qkv.cstruct(), self.out.cstruct(), self.up.cstruct(),
-                      self.down.cstruct())
+                      self.down.cstruct(), gate)
 
 
 def pack_block(W: dict, bits: int, D: int, F: int) -> Block:
-    return Block(D, F, *(pack(np.asarray(W[k]), bits) for k in ("qkv", "out", "up", "down")))
+    """Pack qkv, out, up, down (and gate, when W has one)."""
+    ws = {k: pack(np.asarray(W[k]), bits) for k in ("qkv", "out", "up", "down")}
+    gate = pack(np.asarray(W["gate"]), bits) if "gate" in W else None
+    return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], gate)
+
+
+def silu(z: float) -> float:
+    """silu(z) = z / (1 + e^-z) in FP64 (or_silu)."""
+    return lib().or_silu(float(z))
 
 
 def loop_range(blk: Block, h, L0: int, L1: int):
     """Apply iterations [L0, L1) to a copy of FP64 h [M][D].  Returns (h, last)
-    where last holds the final iteration's FP16-valued norm, qkv, u and y."""
+    where last holds the final iteration's FP16-valued norm, qkv, u (the FFN
+    hidden: the up output, or fp16(silu(g) * u) when gated), y and, when
+    gated, g."""
     h = np.array(h, dtype=np.float64, order="C", copy=True)
     M = h.shape[0]
     last = {"norm": np.zeros((M, blk.D)), "qkv": np.zeros((M, 3 * blk.D)),
-            "u": np.zeros((M, blk.F)), "y": np.zeros((M, blk.D))}
+            "u": np.zeros((M, blk.F)), "y": np.zeros((M, blk.D)), "g": np.zeros((M, blk.F))}
     b = blk.cstruct()
     _check("loop_range", lib().or_loop_range(C.byref(b), _ptr(h), M, L0, L1, _ptr(last["norm"]),
                                              _ptr(last["qkv"]), _ptr(last["u"]),
-                                             _ptr(last["y"])))
+                                             _ptr(last["y"]), _ptr(last["g"])))
+    if blk.gate is None:
+        del last["g"]
     return h, last

@@ -31,7 +31,8 @@
  *  - layout: codes [N][K*b/32] uint32, scales/zeros [N][K/G] FP16, N-major;
  *  - glue between the projections: parameter-free LayerNorm (eps 1e-5,
  *    population variance), self-only attention (the V slice of qkv, columns
- *    [2D, 3D)), identity FFN activation; FP16 rounding at the LN outputs and at
+ *    [2D, 3D)), identity FFN activation (or SwiGLU when the block has a gate
+ *    weight, see or_block); FP16 rounding at the LN outputs and at
  *    every GEMM output, FP64 residual.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
@@ -328,10 +329,22 @@ int or_layernorm(const double* h, int32_t M, int32_t D, double* out)
 
 /* ---------------------------------------------------------------- loop --- */
 
+/* The block's weights.  gate.codes == NULL: four projections, identity FFN
+ * activation.  Otherwise the FFN is SwiGLU ("Model" page, Parameters:
+ * ffn_dim is the width of the gate and up projections; "β-Informed Deployment
+ * Features" page, CTX-TIER Phase 2: the loop block's five weights attn_qkv,
+ * attn_out, mlp_gate, mlp_up, mlp_down): a = fp16(silu(g) * u) with
+ * g = fp16(x . Wgate), u = fp16(x . Wup), then down(a). */
 typedef struct {
     int32_t D, F;
-    or_weight qkv, out, up, down;
+    or_weight qkv, out, up, down, gate;
 } or_block;
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z), in FP64. */
+double or_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
 
 static void round_all(double* v, int64_t n)
 {
@@ -350,13 +363,16 @@ static void round_all(double* v, int64_t n)
  * FP16-valued intermediates: norm (the second LN output), qkv, u and d. */
 int or_loop_range(const or_block* b, double* h, int32_t M, int32_t L0,
                   int32_t L1, double* last_norm, double* last_qkv,
-                  double* last_u, double* last_y)
+                  double* last_u, double* last_y, double* last_g)
 {
     const int32_t D = b->D, F = b->F;
+    const int gated = b->gate.codes != NULL;
     if (M < 0 || L0 < 0 || L1 < L0 || D <= 0 || F <= 0)
         return OR_EINVAL;
     if (b->qkv.K != D || b->qkv.N != 3 * D || b->out.K != D || b->out.N != D ||
         b->up.K != D || b->up.N != F || b->down.K != F || b->down.N != D)
+        return OR_EINVAL;
+    if (gated && (b->gate.K != D || b->gate.N != F))
         return OR_EINVAL;
     if (M == 0 || L0 == L1)
         return OR_OK;
@@ -366,7 +382,8 @@ int or_loop_range(const or_block* b, double* h, int32_t M, int32_t L0,
     double* v = (double*)malloc(sizeof(double) * md);
     double* o = (double*)malloc(sizeof(double) * md);
     double* u = (double*)malloc(sizeof(double) * (size_t)M * F);
-    int st = (x && qkv && v && o && u) ? OR_OK : OR_ENOMEM;
+    double* g = gated ? (double*)malloc(sizeof(double) * (size_t)M * F) : NULL;
+    int st = (x && qkv && v && o && u && (g || !gated)) ? OR_OK : OR_ENOMEM;
     for (int32_t l = L0; l < L1 && st == OR_OK; ++l) {
         or_layernorm(h, M, D, x);
         st = gemm_d(x, D, M, &b->qkv, qkv, 3 * D);
@@ -386,6 +403,14 @@ int or_loop_range(const or_block* b, double* h, int32_t M, int32_t L0,
         if (st)
             break;
         round_all(u, (int64_t)M * F);
+        if (gated) {
+            st = gemm_d(x, D, M, &b->gate, g, F);
+            if (st)
+                break;
+            round_all(g, (int64_t)M * F);
+            for (int64_t i = 0; i < (int64_t)M * F; ++i)
+                u[i] = or_round_half(or_silu(g[i]) * u[i]);
+        }
         st = gemm_d(u, F, M, &b->down, o, D);
         if (st)
             break;
@@ -402,12 +427,15 @@ int or_loop_range(const or_block* b, double* h, int32_t M, int32_t L0,
             memcpy(last_u, u, sizeof(double) * (size_t)M * F);
         if (last_y)
             memcpy(last_y, o, sizeof(double) * md);
+        if (last_g && gated)
+            memcpy(last_g, g, sizeof(double) * (size_t)M * F);
     }
     free(x);
     free(qkv);
     free(v);
     free(o);
     free(u);
+    free(g);
     return st;
 }
 

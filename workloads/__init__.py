@@ -9,7 +9,8 @@ Deployment Features" page (CTX-TIER section: the loop block's projections) and
 the "Model" page (config() example: dim 2048, ffn_dim 8192, default_loops 8).
 Weights stand in for a GPTQ artifact: W ~ N(0, 0.02) FP32, activations
 X ~ N(0, 1) rounded to FP16.  Draw order for a block: Wqkv, Wout, Wup, Wdown,
-then X.
+then X; a gated (SwiGLU) block draws the pages' five weights in their order,
+Wqkv, Wout, Wgate, Wup, Wdown, then X.
 """
 from __future__ import annotations
 
@@ -39,8 +40,10 @@ def activations(M: int, K: int, g: torch.Generator) -> torch.Tensor:
     return torch.randn(M, K, generator=g, dtype=torch.float32).to(torch.float16)
 
 
-def block_shapes(D: int = D_MODEL, F: int = D_FFN) -> dict[str, tuple[int, int]]:
-    """(K, N) of the four loop-block projections, in draw order."""
+def block_shapes(D: int = D_MODEL, F: int = D_FFN, gated: bool = False) -> dict[str, tuple[int, int]]:
+    """(K, N) of the loop-block projections, in draw order."""
+    if gated:
+        return {"qkv": (D, 3 * D), "out": (D, D), "gate": (D, F), "up": (D, F), "down": (F, D)}
     return {"qkv": (D, 3 * D), "out": (D, D), "up": (D, F), "down": (F, D)}
 
 
@@ -52,9 +55,10 @@ class BlockInputs:
     X: torch.Tensor  # FP16 [M][D]
 
 
-def block(M: int, seed: int = 0, D: int = D_MODEL, F: int = D_FFN) -> BlockInputs:
+def block(M: int, seed: int = 0, D: int = D_MODEL, F: int = D_FFN,
+          gated: bool = False) -> BlockInputs:
     g = generator(seed)
-    W = {name: weight(K, N, g) for name, (K, N) in block_shapes(D, F).items()}
+    W = {name: weight(K, N, g) for name, (K, N) in block_shapes(D, F, gated).items()}
     X = activations(M, D, g)
     return BlockInputs(D=D, F=F, W=W, X=X)
 
