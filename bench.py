@@ -47,8 +47,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def block_flops(M: int, D: int = D, F: int = F) -> float:
-    return 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
+def block_flops(M: int, D: int = D, F: int = F, gated: bool = False) -> float:
+    return 2.0 * M * (D * 3 * D + D * D + (2 if gated else 1) * D * F + F * D)
 
 
 def time_loop(qg, torch, blk, h, L, scratch, steps, warmup):
@@ -235,8 +235,8 @@ def extra_legs(qg, torch, workloads, args):
     del pool
     sync()
 
-    def loop_case(name, bits, M, L):
-        inp = workloads.block(M, seed=0)
+    def loop_case(name, bits, M, L, gated=False):
+        inp = workloads.block(M, seed=0, gated=gated)
         blk = qg.pack_block(inp.W, bits, D, F)
         scratch = qg.alloc_loop_scratch(blk, M)
         h = inp.X.float().to(dev)
@@ -245,7 +245,9 @@ def extra_legs(qg, torch, workloads, args):
         per = time_loop(qg, torch, blk, h, L, scratch, reps, 1) / reps
         r = {"M": M, "L": L, "bits": bits, "ms_per_call": round(per * 1e3, 4),
              "eff_weight_GB/s": round(L * blk.nbytes() / per / 1e9, 1),
-             "TFLOP/s": round(block_flops(M) * L / per / 1e12, 2)}
+             "TFLOP/s": round(block_flops(M, gated=gated) * L / per / 1e12, 2)}
+        if gated:
+            r["ffn"] = "swiglu"
         r["frac_hbm"] = round(r["eff_weight_GB/s"] / HBM_PEAK_GBS, 4)
         r["frac_mfma"] = round(r["TFLOP/s"] / MFMA_F16_PEAK_TFLOPS, 4)
         out[name] = r
@@ -279,6 +281,9 @@ def extra_legs(qg, torch, workloads, args):
     loop_case("c4a_int2_block_m1_l16", 2, 1, 16)
     loop_case("c4b_int2_block_m128_l8", 2, 128, 8)
     loop_case("c5a_int4_block_m16_l32", 4, 16, 32)
+    # SwiGLU block (gate projection D x F added): decode and prefill.
+    loop_case("next2_int4_gated_block_m1_l8", 4, 1, 8, gated=True)
+    loop_case("next2_int4_gated_block_m512_l8", 4, 512, 8, gated=True)
 
     # c5b: M=2048 single-shot prefill through the down projection K=8192 -> N=2048.
     W, X = workloads.single_gemm(2048, 8192, 2048, seed=0)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 1
+#define QG_ABI_VERSION 2
 #define QG_LAYOUT_VERSION 1
 
 /* Status codes.  EINVAL: bad argument (the pages' ValueError); EUNSUPPORTED:
@@ -77,6 +77,15 @@ typedef struct qg_weight {
 /* The loop block's four projections (CTX-TIER Phase 2b names the block's
  * attn_qkv, attn_out, mlp_up and mlp_down weights): qkv K=D, N=3D; out K=D,
  * N=D; up K=D, N=F; down K=F, N=D.  Each weight carries its own bits. */
+/* The looped block's weights.  gate.codes == NULL (all of gate zero): four
+ * projections and the identity FFN activation.  Otherwise gate is the fifth
+ * weight of the pages' block (mlp_gate; "β-Informed Deployment Features"
+ * page, CTX-TIER Phase 2 lists attn_qkv, attn_out, mlp_gate, mlp_up,
+ * mlp_down) with the shape of up (K = D, N = F), and the FFN is SwiGLU
+ * ("Model" page, Parameters: ffn_dim is the width of the gate and up
+ * projections): a = fp16(silu(g) * u), g = fp16(x . Wgate),
+ * u = fp16(x . Wup), silu(z) = z / (1 + e^-z) evaluated in FP32.  Each weight
+ * carries its own bits. */
 typedef struct qg_block {
     int32_t D;
     int32_t F;
@@ -84,6 +93,7 @@ typedef struct qg_block {
     qg_weight out;
     qg_weight up;
     qg_weight down;
+    qg_weight gate;
 } qg_block;
 
 int qg_abi_version(void);
@@ -134,20 +144,23 @@ size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M);
  * the same weights are applied on every iteration).  Per iteration:
  *   x = fp16(LN(h)); qkv = fp16(x . Wqkv); o = fp16(qkv[:, 2D:3D] . Wout);
  *   h += o; x = fp16(LN(h)); u = fp16(x . Wup); d = fp16(u . Wdown); h += d;
+ * and with a gate weight u = fp16(silu(fp16(x . Wgate)) * fp16(x . Wup)).
  * LN is parameter-free, eps 1e-5, population variance, computed in FP32.
  * Requires 0 <= L0 <= L1; L0 == L1 (or M == 0) is a no-op.  [L0, L1) followed
  * by [L1, L2) gives the same bits as [L0, L2).
  * scratch: device buffer of at least qg_loop_scratch_bytes(blk, M) bytes; after
  * the call it holds the last iteration's FP16 intermediates at the offsets
  * given by qg_loop_scratch_offsets (norm = second LN output [M][D],
- * qkv [M][3D], u [M][F], y = last down-projection output [M][D]). */
+ * qkv [M][3D], u [M][F] = the down projection's input, y = last
+ * down-projection output [M][D], and with a gate g = gate output [M][F]). */
 int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
                   void* scratch, size_t scratch_bytes, void* stream);
 size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M);
-/* Byte offsets of norm, qkv, u and y inside the loop scratch (any pointer may
- * be NULL).  Returns QG_EINVAL for a bad block. */
+/* Byte offsets of norm, qkv, u, y and g inside the loop scratch (any pointer
+ * may be NULL; g is 0 for a block without a gate).  Returns QG_EINVAL for a
+ * bad block. */
 int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t* qkv,
-                            size_t* u, size_t* y);
+                            size_t* u, size_t* y, size_t* g);
 
 /* Test exports running the same device unpack/dequant code the GEMM kernels
  * use.  qg_unpack writes codes q [N][K] as uint8.  qg_dequant writes

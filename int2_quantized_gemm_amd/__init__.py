@@ -39,7 +39,8 @@ class _Weight(C.Structure):
 
 class _Block(C.Structure):
     _fields_ = [("D", C.c_int32), ("F", C.c_int32),
-                ("qkv", _Weight), ("out", _Weight), ("up", _Weight), ("down", _Weight)]
+                ("qkv", _Weight), ("out", _Weight), ("up", _Weight), ("down", _Weight),
+                ("gate", _Weight)]
 
 
 def _load():
@@ -61,6 +62,7 @@ def _load():
         "qg_loop_range": (C.c_int, [B, vp, i32, i32, i32, vp, sz, vp]),
         "qg_loop_scratch_bytes": (sz, [B, i32]),
         "qg_loop_scratch_offsets": (C.c_int, [B, i32, C.POINTER(sz), C.POINTER(sz),
+                                              C.POINTER(sz),
                                               C.POINTER(sz), C.POINTER(sz)]),
         "qg_unpack": (C.c_int, [W, vp, vp]),
         "qg_dequant": (C.c_int, [W, i32, vp, vp]),
@@ -181,19 +183,30 @@ def qg_gemm_int2(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None
 
 @dataclass
 class Block:
+    """The loop block's packed projections; gate None means four projections
+    and the identity FFN activation, otherwise the FFN is SwiGLU."""
     D: int
     F: int
     qkv: PackedWeight
     out: PackedWeight
     up: PackedWeight
     down: PackedWeight
+    gate: PackedWeight | None = None
+
+    def weights(self) -> dict:
+        ws = {"qkv": self.qkv, "out": self.out, "up": self.up, "down": self.down}
+        if self.gate is not None:
+            ws["gate"] = self.gate
+        return ws
 
     def cstruct(self) -> _Block:
+        gate = self.gate.cstruct() if self.gate is not None else _Weight(0, 0, 0, 0, None, None,
+                                                                           None)
         return _Block(self.D, self.F, self.qkv.cstruct(), self.out.cstruct(), self.up.cstruct(),
-                      self.down.cstruct())
+                      self.down.cstruct(), gate)
 
     def nbytes(self) -> int:
-        return sum(w.nbytes() for w in (self.qkv, self.out, self.up, self.down))
+        return sum(w.nbytes() for w in self.weights().values())
 
 
 def qg_loop_scratch_bytes(blk: Block, M: int) -> int:
@@ -203,10 +216,10 @@ def qg_loop_scratch_bytes(blk: Block, M: int) -> int:
 
 def qg_loop_scratch_offsets(blk: Block, M: int) -> dict:
     b = blk.cstruct()
-    vals = [C.c_size_t() for _ in range(4)]
+    vals = [C.c_size_t() for _ in range(5)]
     _check("qg_loop_scratch_offsets",
            lib.qg_loop_scratch_offsets(C.byref(b), M, *(C.byref(v) for v in vals)))
-    return dict(zip(("norm", "qkv", "u", "y"), (v.value for v in vals)))
+    return dict(zip(("norm", "qkv", "u", "y", "g"), (v.value for v in vals)))
 
 
 def alloc_loop_scratch(blk: Block, M: int, device="cuda") -> torch.Tensor:
@@ -217,6 +230,8 @@ def scratch_views(blk: Block, M: int, scratch: torch.Tensor) -> dict:
     """FP16 views of the last iteration's intermediates inside a loop scratch."""
     off = qg_loop_scratch_offsets(blk, M)
     shapes = {"norm": (M, blk.D), "qkv": (M, 3 * blk.D), "u": (M, blk.F), "y": (M, blk.D)}
+    if blk.gate is not None:
+        shapes["g"] = (M, blk.F)
     out = {}
     for k, shp in shapes.items():
         n = shp[0] * shp[1]
@@ -291,16 +306,14 @@ def requant_block(blk: Block, in_place: bool = False, stream=None) -> Block:
     (INT2 ones are kept).  Each call has synchronised the stream when it
     returns, so the INT4 tensors may be dropped (out of place) as soon as the
     caller releases `blk`."""
-    ws = {}
-    for k in ("qkv", "out", "up", "down"):
-        w = getattr(blk, k)
-        ws[k] = qg_requant_4to2(w, in_place=in_place, stream=stream) if w.bits == 4 else w
-    return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"])
+    ws = {k: qg_requant_4to2(w, in_place=in_place, stream=stream) if w.bits == 4 else w
+          for k, w in blk.weights().items()}
+    return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))
 
 
 def pack_block(W: dict, bits: int, D: int, F: int, device="cuda") -> Block:
-    """qg_pack each of the four FP32 [K][N] projection weights of a block."""
-    ws = {}
-    for k in ("qkv", "out", "up", "down"):
-        ws[k] = qg_pack(W[k].to(device=device, dtype=torch.float32).contiguous(), bits)
-    return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"])
+    """qg_pack each FP32 [K][N] projection weight of a block (qkv, out, up,
+    down, and gate when W has one)."""
+    ws = {k: qg_pack(W[k].to(device=device, dtype=torch.float32).contiguous(), bits)
+          for k in ("qkv", "out", "up", "down", "gate") if k in W}
+    return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))

@@ -125,6 +125,34 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) { return (double)(
 // Round an FP32 accumulator to FP16 (round to nearest even).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((f16)v); }
 
+// ---- output epilogue shared by every GEMM kernel.  The FP32 accumulator is
+// rounded to FP16 (y16), then
+//   kStore:    Y[m][n] = y16
+//   kResidual: Y[m][n] = y16 and h[m][n] += float(y16)          (h FP32 [.][ldh])
+//   kGateMul:  Y[m][n] = fp16(silu(g[m][n]) * y16), silu(z) = z / (1 + e^-z)
+//              in FP32 (g FP16 [.][ldg]: the gate projection of a SwiGLU FFN)
+enum Epilogue { kStore = 0, kResidual = 1, kGateMul = 2 };
+
+struct OutEpi {
+    uint16_t* Y;
+    int64_t ldy;
+    float* h;
+    int64_t ldh;
+    const uint16_t* g;
+    int64_t ldg;
+    int kind;
+};
+
+__device__ __forceinline__ void epi_store(const OutEpi& e, int64_t m, int64_t n, float acc) {
+    uint16_t y = f32_to_f16_bits(acc);
+    if (e.kind == kGateMul) {
+        const float gv = (float)as_f16(e.g[m * e.ldg + n]);
+        y = f32_to_f16_bits(gv / (1.0f + expf(-gv)) * (float)as_f16(y));
+    }
+    e.Y[m * e.ldy + n] = y;
+    if (e.kind == kResidual) e.h[m * e.ldh + n] += (float)as_f16(y);
+}
+
 }  // namespace qg
 
 namespace qg {

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/qgemm.h"
+#include "device.h"
 
 namespace qg {
 
@@ -19,11 +20,7 @@ hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in
                                int* status, hipStream_t s);
 hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s);
 
-// ---- GEMM (kernels_gemm.hip)
-// Epilogue applied to the FP16-rounded output y16 of each element:
-//   kStore:    Y[m][n] = y16
-//   kResidual: Y[m][n] = y16 and h[m][n] += float(y16)   (h FP32 [M][ldh])
-enum Epilogue { kStore = 0, kResidual = 1 };
+// ---- GEMM (kernels_gemm.hip); the epilogue kinds are in device.h.
 
 struct GemmArgs {
     const qg_half* X;
@@ -42,7 +39,11 @@ struct GemmArgs {
     // norm_out, if set, receives them.
     const float* ln_h = nullptr;
     qg_half* norm_out = nullptr;
+    // kGateMul: the gate projection g [M][ldg] (FP16) the output multiplies.
+    const qg_half* gm = nullptr;
+    int64_t ldg = 0;
 
+    OutEpi out() const { return OutEpi{Y, ldy, h, ldh, gm, ldg, (int)epi}; }
 };
 
 // True when a GEMM of this shape can take its activations as the fused

@@ -104,8 +104,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                                               const uint32_t* __restrict__ codes,
                                               const uint16_t* __restrict__ scales,
                                               const uint16_t* __restrict__ zeros, int N,
-                                              uint16_t* __restrict__ Y, float* __restrict__ h,
-                                              int epi) {
+                                              OutEpi out) {
     using F = Fmt<BITS>;
     using G = GemvMath<BITS>;
     constexpr int RPW = 64 / LPR;
@@ -236,11 +235,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         }
         acc = segment_sum<LPR>(acc);
         const int row = row0 + u * RPW + rsub;
-        if (sub == 0 && row < N) {
-            const uint16_t y = f32_to_f16_bits(acc);
-            Y[row] = y;
-            if (epi == kResidual) h[row] += (float)as_f16(y);
-        }
+        if (sub == 0 && row < N) epi_store(out, 0, row, acc);
     }
 }
 
@@ -298,13 +293,6 @@ __device__ __forceinline__ void load_a(const uint16_t* xrow, bool valid, int g, 
     }
 }
 
-__device__ __forceinline__ void store_out(uint16_t* Y, int64_t ldy, float* h, int64_t ldh, int epi,
-                                          int m, int n, float v) {
-    const uint16_t y = f32_to_f16_bits(v);
-    Y[(int64_t)m * ldy + n] = y;
-    if (epi == kResidual) h[(int64_t)m * ldh + n] += (float)as_f16(y);
-}
-
 // ---------------------------------------------------------------- skinny ----
 
 // 2 <= M <= 16.  A workgroup of four waves computes 16 output channels over
@@ -326,8 +314,7 @@ template <int BITS>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N, int S,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
-    float* __restrict__ part) {
+    OutEpi out, float* __restrict__ part) {
     constexpr int kMaxGpw = kSkinnyMaxK / kGroup / 4;  // groups per wave
     __shared__ __attribute__((aligned(1024))) uint8_t xs[16 * kSkinnyMaxK * 2];
     __shared__ f32x4 red[4][64];
@@ -398,7 +385,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         if (part != nullptr)
             part[(int64_t)p * M * N + (int64_t)m * N + n] = sum[r];
         else
-            store_out(Y, ldy, h, ldh, epi, m, n, sum[r]);
+            epi_store(out, m, n, sum[r]);
     }
 }
 
@@ -439,7 +426,7 @@ hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     const int waves = (steps + U - 1) / U;
     const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     k_gemv<BITS, LPR, CPR, U, LN><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
-        a.X, a.ln_h, a.norm_out, a.w->codes, a.w->scales, a.w->zeros, N, a.Y, a.h, (int)a.epi);
+        a.X, a.ln_h, a.norm_out, a.w->codes, a.w->scales, a.w->zeros, N, a.out());
     return hipGetLastError();
 }
 
@@ -499,8 +486,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((a.w->N + 15) / 16, S);
     float* part = S > 1 ? (float*)a.ws : nullptr;
     k_gemm_skinny<BITS><<<grid, 256, 0, s>>>(a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros,
-                                             a.w->K, a.w->N, S, a.Y, a.ldy, a.h, a.ldh,
-                                             (int)a.epi, part);
+                                             a.w->K, a.w->N, S, a.out(), part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     return launch_splitk_reduce(part, S, a, s);

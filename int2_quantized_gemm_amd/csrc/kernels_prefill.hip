@@ -77,8 +77,7 @@ template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int ST
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefill(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
-    int groups_per_part, float* __restrict__ part) {
+    OutEpi out, int groups_per_part, float* __restrict__ part) {
     using C = Cfg<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES>;
     __shared__ __attribute__((aligned(16))) f16 lds[C::LDS_HALVES];
 
@@ -245,11 +244,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * C::WTM + 32 * im + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (m < M) {
-                const uint16_t y = f32_to_f16_bits(v[r]);
-                Y[(int64_t)m * ldy + n] = y;
-                if (epi == kResidual) h[(int64_t)m * ldh + n] += (float)as_f16(y);
-            }
+            if (m < M) epi_store(out, m, n, v[r]);
         }
     };
 
@@ -391,8 +386,7 @@ template <int BITS, int BM, int RA, int RBS>
 __global__ __launch_bounds__(256) void k_gemm_ring(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    uint16_t* __restrict__ Y, int64_t ldy, float* __restrict__ h, int64_t ldh, int epi,
-    int groups_per_part, float* __restrict__ part, Raster rs) {
+    OutEpi out, int groups_per_part, float* __restrict__ part, Raster rs) {
     using F = Fmt<BITS>;
     using RB = RingB<BITS>;
     constexpr int TM = BM / 32;
@@ -573,23 +567,18 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         for (int r = 0; r < 16; ++r) {
             const int m = m0 + 32 * tm + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (m >= M) continue;
-            if (part != nullptr) {
+            if (part != nullptr)
                 part[(int64_t)blockIdx.z * M * N + (int64_t)m * N + n] = acc[tm][r];
-            } else {
-                const uint16_t y = f32_to_f16_bits(acc[tm][r]);
-                Y[(int64_t)m * ldy + n] = y;
-                if (epi == kResidual) h[(int64_t)m * ldh + n] += (float)as_f16(y);
-            }
+            else
+                epi_store(out, m, n, acc[tm][r]);
         }
     }
 }
 
-// Sum of the K-split partial tiles part[0..S)[M][N] in split order, rounded to
-// FP16, with the optional residual epilogue.  Four elements per thread.
+// Sum of the K-split partial tiles part[0..S)[M][N] in split order, then the
+// output epilogue.  Four elements per thread.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
-                                                       int M, int N, uint16_t* __restrict__ Y,
-                                                       int64_t ldy, float* __restrict__ h,
-                                                       int64_t ldh, int epi) {
+                                                       int M, int N, OutEpi out) {
     const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     const int64_t total = (int64_t)M * N;
     if (i4 >= total) return;
@@ -600,10 +589,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
         if (i >= total) break;
         float v = part[i];
         for (int z = 1; z < S; ++z) v += part[z * plane + i];
-        const int64_t m = i / N, n = i % N;
-        const uint16_t y = f32_to_f16_bits(v);
-        Y[m * ldy + n] = y;
-        if (epi == kResidual) h[m * ldh + n] += (float)as_f16(y);
+        epi_store(out, i / N, i % N, v);
     }
 }
 
@@ -659,8 +645,8 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
     float* part = split > 1 ? (float*)a.ws : nullptr;
     k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
-        a.ldh, (int)a.epi, a.w->K / kBK / split, part);
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
+        a.w->K / kBK / split, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || split == 1) return e;
     return reduce_parts(a, split, part, s);
@@ -675,8 +661,8 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
     float* part = split > 1 ? (float*)a.ws : nullptr;
     k_gemm_ring<BITS, BM, RA, RBS><<<grid, 256, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.Y, a.ldy, a.h,
-        a.ldh, (int)a.epi, a.w->K / kBK / split, part, rs);
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
+        a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || split == 1) return e;
     return reduce_parts(a, split, part, s);
@@ -701,8 +687,7 @@ hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_splitk_reduce(const float* part, int S, const GemmArgs& a, hipStream_t s) {
     const int64_t total = (int64_t)a.M * a.w->N;
     const unsigned blocks = (unsigned)((total + 4 * 256 - 1) / (4 * 256));
-    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, S, a.M, a.w->N, a.Y, a.ldy, a.h, a.ldh,
-                                           (int)a.epi);
+    k_splitk_reduce<<<blocks, 256, 0, s>>>(part, S, a.M, a.w->N, a.out());
     return hipGetLastError();
 }
 

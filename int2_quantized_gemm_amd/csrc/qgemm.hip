@@ -97,8 +97,10 @@ int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half*
 // ---- loop scratch layout: norm [M][D], qkv [M][3D], u [M][F], y [M][D] (FP16),
 // then the GEMM workspace; every region 256-byte aligned.
 struct LoopLayout {
-    size_t norm, qkv, u, y, ws, ws_bytes, total;
+    size_t norm, qkv, u, y, g, ws, ws_bytes, total;
 };
+
+bool gated(const qg_block* b) { return b->gate.codes != nullptr; }
 
 LoopLayout loop_layout(const qg_block* b, int32_t M) {
     LoopLayout L{};
@@ -107,10 +109,12 @@ LoopLayout loop_layout(const qg_block* b, int32_t M) {
     L.qkv = align_up(L.norm + m * b->D * 2, 256);
     L.u = align_up(L.qkv + m * 3 * b->D * 2, 256);
     L.y = align_up(L.u + m * b->F * 2, 256);
-    L.ws = align_up(L.y + m * b->D * 2, 256);
+    L.g = gated(b) ? align_up(L.y + m * b->D * 2, 256) : 0;
+    L.ws = align_up((gated(b) ? L.g + m * b->F * 2 : L.y + m * b->D * 2), 256);
     size_t ws = 0;
-    const qg_weight* ws_list[4] = {&b->qkv, &b->out, &b->up, &b->down};
+    const qg_weight* ws_list[5] = {&b->qkv, &b->out, &b->up, &b->down, &b->gate};
     for (const qg_weight* w : ws_list) {
+        if (w == &b->gate && !gated(b)) continue;
         const size_t n = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
         ws = n > ws ? n : ws;
     }
@@ -130,11 +134,13 @@ int check_block(const qg_block* b, const char* fn) {
         const qg_weight* w;
         const char* name;
         int K, N;
-    } ws[4] = {{&b->qkv, "qkv", b->D, 3 * b->D},
+    } ws[5] = {{&b->qkv, "qkv", b->D, 3 * b->D},
                {&b->out, "out", b->D, b->D},
                {&b->up, "up", b->D, b->F},
-               {&b->down, "down", b->F, b->D}};
+               {&b->down, "down", b->F, b->D},
+               {&b->gate, "gate", b->D, b->F}};
     for (auto& e : ws) {
+        if (e.w == &b->gate && !gated(b)) continue;  // no gate: identity FFN activation
         int st = check_weight(e.w, fn, e.name);
         if (st) return st;
         if (e.w->K != e.K || e.w->N != e.N)
@@ -155,11 +161,12 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     void* ws = base + L.ws;
     const int D = blk->D, F = blk->F;
     hipError_t e = hipSuccess;
-    // At M == 1 the QKV and up GEMVs compute the LayerNorm of h in their
-    // prologue (the up GEMV also stores it as the scratch norm); otherwise a
-    // LayerNorm kernel writes norm first.
+    // At M == 1 the QKV GEMV computes the LayerNorm of h in its prologue;
+    // otherwise a LayerNorm kernel writes norm first.
+    const bool gate = gated(blk);
+    qg_half* g = gate ? (qg_half*)(base + L.g) : nullptr;
     const bool fuse_qkv = qg::gemm_fuses_layernorm(blk->qkv.bits, M, D, 3 * D);
-    const bool fuse_up = qg::gemm_fuses_layernorm(blk->up.bits, M, D, F);
+    const bool fuse_first = qg::gemm_fuses_layernorm(gate ? blk->gate.bits : blk->up.bits, M, D, F);
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
         qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
         if (fuse_qkv)
@@ -171,14 +178,25 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
             e = qg::launch_gemm({qkv + 2 * D, 3 * D, &blk->out, y, D, M, qg::kResidual, h, D, ws,
                                  L.ws_bytes},
                                 s);
-        qg::GemmArgs ua{norm, D, &blk->up, u, F, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
-        if (fuse_up) {
-            ua.ln_h = h;
-            ua.norm_out = norm;
+        // FFN input: the first FFN projection (gate, else up) normalises h
+        // itself at M == 1 and stores norm; otherwise a LayerNorm kernel
+        // writes norm first.  With a gate, up multiplies silu(g) in.
+        const qg_weight* first = gate ? &blk->gate : &blk->up;
+        qg::GemmArgs fa{norm, D, first, gate ? g : u, F, M, qg::kStore, nullptr, 0, ws,
+                        L.ws_bytes};
+        if (fuse_first) {
+            fa.ln_h = h;
+            fa.norm_out = norm;
         } else if (e == hipSuccess) {
             e = qg::launch_layernorm(h, M, D, norm, s);
         }
-        if (e == hipSuccess) e = qg::launch_gemm(ua, s);
+        if (e == hipSuccess) e = qg::launch_gemm(fa, s);
+        if (gate && e == hipSuccess) {
+            qg::GemmArgs ua{norm, D, &blk->up, u, F, M, qg::kGateMul, nullptr, 0, ws, L.ws_bytes};
+            ua.gm = g;
+            ua.ldg = F;
+            e = qg::launch_gemm(ua, s);
+        }
         if (e == hipSuccess)
             e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
                                 s);
@@ -426,7 +444,7 @@ size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M) {
 }
 
 int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t* qkv, size_t* u,
-                            size_t* y) {
+                            size_t* y, size_t* g) {
     int st = check_block(blk, "qg_loop_scratch_offsets");
     if (st) return st;
     if (M < 0) return fail(QG_EINVAL, "qg_loop_scratch_offsets: M = %d must be >= 0", M);
@@ -435,6 +453,7 @@ int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t
     if (qkv) *qkv = L.qkv;
     if (u) *u = L.u;
     if (y) *y = L.y;
+    if (g) *g = L.g;
     return ok();
 }
 

@@ -29,10 +29,10 @@ def test_header_functions_are_exported():
 
 
 def test_versions():
-    assert qg.qg_abi_version() == 1
+    assert qg.qg_abi_version() == 2
     assert qg.qg_layout_version() == 1
     text = open(HEADER).read()
-    assert "#define QG_ABI_VERSION 1" in text and "#define QG_LAYOUT_VERSION 1" in text
+    assert "#define QG_ABI_VERSION 2" in text and "#define QG_LAYOUT_VERSION 1" in text
 
 
 def _w(bits=4, K=2048, N=2048, group=128, codes=FAKE, scales=FAKE, zeros=FAKE):
@@ -81,9 +81,10 @@ def test_gemm_m0_is_a_noop_without_device_work():
 
 
 def _block(D=256, F=512, bits=4, **over):
-    ws = dict(qkv=_w(bits, D, 3 * D), out=_w(bits, D, D), up=_w(bits, D, F), down=_w(bits, F, D))
+    ws = dict(qkv=_w(bits, D, 3 * D), out=_w(bits, D, D), up=_w(bits, D, F), down=_w(bits, F, D),
+              gate=qg._Weight(0, 0, 0, 0, None, None, None))
     ws.update(over)
-    return qg._Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"])
+    return qg._Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws["gate"])
 
 
 def _loop(b, h=FAKE, M=1, L0=0, L1=1, scratch=FAKE, nbytes=1 << 30):
@@ -98,6 +99,9 @@ def test_loop_validation():
     assert _loop(_block(out=_w(4, 256, 128))) == qg.QG_EINVAL and "out" in qg.qg_last_error()
     assert _loop(_block(D=200)) == qg.QG_EINVAL
     assert _loop(_block(up=_w(3, 256, 512))) == qg.QG_EUNSUPPORTED
+    # a gate, when present, must have the shape of up
+    assert _loop(_block(gate=_w(4, 256, 256))) == qg.QG_EINVAL and "gate" in qg.qg_last_error()
+    assert _loop(_block(gate=_w(2, 256, 512)), L0=3, L1=3) == qg.QG_OK
     need = qg.lib.qg_loop_scratch_bytes(C.byref(b), 4)
     assert need > 0
     assert _loop(b, M=4, nbytes=need - 1) == qg.QG_EINVAL and "scratch" in qg.qg_last_error()
@@ -108,15 +112,22 @@ def test_loop_validation():
     assert _loop(b, M=0) == qg.QG_OK
 
 
-def test_loop_scratch_layout_is_documented_and_aligned():
+@pytest.mark.parametrize("gated", [False, True])
+def test_loop_scratch_layout_is_documented_and_aligned(gated):
     D, F, M = 2048, 8192, 512
-    b = _block(D, F)
-    vals = [C.c_size_t() for _ in range(4)]
+    b = _block(D, F, gate=_w(4, D, F)) if gated else _block(D, F)
+    vals = [C.c_size_t() for _ in range(5)]
     assert qg.lib.qg_loop_scratch_offsets(C.byref(b), M, *(C.byref(v) for v in vals)) == 0
-    norm, qkv, u, y = (v.value for v in vals)
+    norm, qkv, u, y, g = (v.value for v in vals)
     assert norm == 0 and qkv >= M * D * 2 and u >= qkv + M * 3 * D * 2 and y >= u + M * F * 2
-    assert all(o % 256 == 0 for o in (norm, qkv, u, y))
-    assert qg.lib.qg_loop_scratch_bytes(C.byref(b), M) >= y + M * D * 2
+    assert all(o % 256 == 0 for o in (norm, qkv, u, y, g))
+    end = y + M * D * 2
+    if gated:
+        assert g >= end
+        end = g + M * F * 2
+    else:
+        assert g == 0
+    assert qg.lib.qg_loop_scratch_bytes(C.byref(b), M) >= end
 
 
 def test_pack_validation():

@@ -19,8 +19,8 @@ qg = pytest.importorskip("int2_quantized_gemm_amd")
 pytestmark = pytest.mark.gpu
 
 
-def _blocks(orc, M, bits, D, F, seed):
-    inp = workloads.block(M, seed=seed, D=D, F=F)
+def _blocks(orc, M, bits, D, F, seed, gated=False):
+    inp = workloads.block(M, seed=seed, D=D, F=F, gated=gated)
     blk = qg.pack_block(inp.W, bits, D, F)
     oblk = orc.pack_block({k: v.numpy() for k, v in inp.W.items()}, bits, D, F)
     return inp, blk, oblk
@@ -31,9 +31,22 @@ def _check_h(h, href, what):
     assert_close(h, href, what, max_abs=1e-2 * max(1.0, rms))
 
 
+def _fp16_ulp(x: float) -> float:
+    return 2.0 ** (np.floor(np.log2(max(x, 2.0 ** -14))) - 10)
+
+
 def _check_scratch(views, last, rows, what):
-    for k in ("norm", "qkv", "u", "y"):
-        assert_close(views[k].float().cpu().numpy()[rows], last[k], f"{what} scratch {k}")
+    for k in ("norm", "qkv", "u", "y", "g"):
+        if k not in last:
+            continue
+        # The SwiGLU activation fp16(silu(g) u) grows past 16 (|a| ~ 25 at
+        # K = 4096), where one FP16 step (1/64) exceeds 1e-2: there max-abs is
+        # two FP16 steps at the largest reference value.
+        max_abs = 1e-2
+        if k == "u" and "g" in last:
+            max_abs = max(1e-2, 2 * _fp16_ulp(float(np.max(np.abs(last[k])))))
+        assert_close(views[k].float().cpu().numpy()[rows], last[k], f"{what} scratch {k}",
+                     max_abs=max_abs)
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -159,4 +172,63 @@ def test_loop_inside_caller_graph_capture(orc):
         assert torch.equal(h, ref), f"captured replay {r}"
         tmp = h0.clone()
         qg.qg_loop_range(blk, tmp, 0, 1, scratch)
+        torch.cuda.synchronize()
+
+
+# SwiGLU blocks (a gate weight): every kernel family takes the gate-multiply
+# epilogue -- GEMV (M=1), skinny (M=3, 16), staged tiled (M=33), ring (M=300),
+# and the split reduction (D=4096: skinny K parts at M=5, tiled K split at
+# M=20).
+GATED = [(1, 256, 640), (3, 256, 640), (16, 256, 640), (33, 256, 640), (300, 2048, 8192),
+         (5, 4096, 256), (20, 4096, 256)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,D,F", GATED)
+def test_loop_gated_block(orc, bits, M, D, F):
+    L = 2
+    inp, blk, oblk = _blocks(orc, M, bits, D, F, seed=M + D, gated=True)
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    rows = slice(None) if M <= 40 else [0, 127, 128, 299]
+    href, last = orc.loop_range(oblk, inp.X.numpy()[rows].astype(np.float64), 0, L)
+    h = h.cpu().numpy()
+    assert np.all(np.isfinite(h))
+    _check_h(h[rows], href, f"gated h bits={bits} M={M} D={D}")
+    _check_scratch(qg.scratch_views(blk, M, scratch), last, rows, f"gated bits={bits} M={M}")
+
+
+@pytest.mark.parametrize("M,L", [(1, 8), (16, 4)])
+def test_loop_gated_measured_block_sampled_rows(orc, M, L):
+    """The pages' five-weight block at D=2048, F=8192 (INT4)."""
+    D, F = workloads.D_MODEL, workloads.D_FFN
+    inp, blk, oblk = _blocks(orc, M, 4, D, F, seed=0, gated=True)
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    rows = [0, M - 1] if M > 1 else [0]
+    href, last = orc.loop_range(oblk, inp.X.numpy()[rows].astype(np.float64), 0, L)
+    _check_h(h.cpu().numpy()[rows], href, f"gated measured M={M}")
+    _check_scratch(qg.scratch_views(blk, M, scratch), last, rows, f"gated measured M={M}")
+
+
+def test_loop_gated_graph_replays_match_direct_enqueue(orc, monkeypatch):
+    D, F, M = 256, 512, 1
+    inp, blk, _ = _blocks(orc, M, 4, D, F, seed=23, gated=True)
+    h0 = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
+    ref = h0.clone()
+    qg.qg_loop_range(blk, ref, 0, 3, scratch)
+    torch.cuda.synchronize()
+    h = torch.empty_like(h0)
+    for r in range(3):
+        monkeypatch.setenv("QG_LOOP_GRAPHS", "1")
+        h.copy_(h0)
+        qg.qg_loop_range(blk, h, 0, 3, scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref), f"graph replay {r}"
+        monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
+        qg.qg_loop_range(blk, h0.clone(), 0, 1, scratch)
         torch.cuda.synchronize()
