@@ -163,7 +163,7 @@ def traffic_from(fetch_csv: str, write_csv: str, command: str):
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(rec_path)) if os.path.exists(rec_path) else {}
     rec[GEMV_KEY] = {
-        "kernel": "k_gemv<4,64,4,2,false> (K=8192, N=2048, M=1)",
+        "kernel": "k_gemv<4,64,4,2,false,1> (K=8192, N=2048, M=1)",
         "source": GEMV_SRC,
         "source_sha256_16": hashlib.sha256(open(src, "rb").read()).hexdigest()[:16],
         "fetch_kib_per_launch_raw": round(med(g_f), 1),
@@ -380,7 +380,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "k_gemv<4,64,4,2,false> (FFN down projection, K=8192, N=2048, M=1)",
+                "kernel": "k_gemv<4,64,4,2,false,1> (FFN down projection, K=8192, N=2048, M=1)",
                 "algorithmic_bytes_per_launch": down_bytes,
                 "avg_launch_us": round(avg_s * 1e6, 3)}
     log(f"roofline: {roofline}")

@@ -143,12 +143,17 @@ struct OutEpi {
     int kind;
 };
 
+// fp16(silu(g) * u) for FP16 bit patterns g and u, in FP32 (the SwiGLU
+// activation; the gate-multiply epilogue and the fused gate-and-up GEMV both
+// use it, so their results agree bit for bit).
+__device__ __forceinline__ uint16_t swiglu_f16(uint16_t g16, uint16_t u16) {
+    const float gv = (float)as_f16(g16);
+    return f32_to_f16_bits(gv / (1.0f + expf(-gv)) * (float)as_f16(u16));
+}
+
 __device__ __forceinline__ void epi_store(const OutEpi& e, int64_t m, int64_t n, float acc) {
     uint16_t y = f32_to_f16_bits(acc);
-    if (e.kind == kGateMul) {
-        const float gv = (float)as_f16(e.g[m * e.ldg + n]);
-        y = f32_to_f16_bits(gv / (1.0f + expf(-gv)) * (float)as_f16(y));
-    }
+    if (e.kind == kGateMul) y = swiglu_f16(e.g[m * e.ldg + n], y);
     e.Y[m * e.ldy + n] = y;
     if (e.kind == kResidual) e.h[m * e.ldh + n] += (float)as_f16(y);
 }

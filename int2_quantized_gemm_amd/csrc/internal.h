@@ -42,6 +42,12 @@ struct GemmArgs {
     // kGateMul: the gate projection g [M][ldg] (FP16) the output multiplies.
     const qg_half* gm = nullptr;
     int64_t ldg = 0;
+    // SwiGLU pair (M == 1 GEMV only, where gemm_fuses_swiglu holds): w is the
+    // gate and w2 the up projection of the same shape and bits; g_out [N]
+    // receives fp16(X . w) and Y fp16(silu(g) * fp16(X . w2)); epi must be
+    // kStore.
+    const qg_weight* w2 = nullptr;
+    qg_half* g_out = nullptr;
 
     OutEpi out() const { return OutEpi{Y, ldy, h, ldh, gm, ldg, (int)epi}; }
 };
@@ -49,6 +55,9 @@ struct GemmArgs {
 // True when a GEMM of this shape can take its activations as the fused
 // LayerNorm of an FP32 row (the M == 1 GEMV path).
 bool gemm_fuses_layernorm(int bits, int M, int K, int N);
+// True when the gate and up projections of this shape can run as one SwiGLU
+// pair launch (GemmArgs::w2).
+bool gemm_fuses_swiglu(int bits, int M, int K, int N);
 
 // Which kernel family and tile a (bits, M, K, N) problem goes to.
 enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };

@@ -97,14 +97,25 @@ struct GemvMath {
 // (mean, then population variance of the centred values, eps 1e-5, reduced
 // by DPP in each wave and then in wave order through LDS), stage it in LDS
 // for the lanes to pick up, and workgroup 0 also writes it to norm_out.
-template <int BITS, int LPR, int CPR, int U, bool LN>
+//
+// NW = 2 is the SwiGLU pair of a gated FFN: weight 0 is the gate and weight 1
+// the up projection, both of the same shape and bits.  Each row step loads
+// the same rows of both, and the lane that finishes row n stores
+// g = fp16(x . Wgate[n]) to gout[n] and fp16(silu(g) * fp16(x . Wup[n])) to
+// out.Y[n] (plain store epilogue), so one launch and one activation pass serve
+// both projections.
+struct GemvWeights {
+    const uint32_t* codes[2];
+    const uint16_t* scales[2];
+    const uint16_t* zeros[2];
+};
+
+template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
 __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                                               const float* __restrict__ hln,
                                               uint16_t* __restrict__ norm_out,
-                                              const uint32_t* __restrict__ codes,
-                                              const uint16_t* __restrict__ scales,
-                                              const uint16_t* __restrict__ zeros, int N,
-                                              OutEpi out) {
+                                              GemvWeights W, int N, OutEpi out,
+                                              uint16_t* __restrict__ gout) {
     using F = Fmt<BITS>;
     using G = GemvMath<BITS>;
     constexpr int RPW = 64 / LPR;
@@ -122,25 +133,27 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
 
     // Issue the weight loads of this wave first; the activations and their
     // LayerNorm are computed while they are in flight.
-    u32x4 wv[U][CPR];
-    uint16_t sv[U][CPR], zv[U][CPR];
+    u32x4 wv[NW][U][CPR];
+    uint16_t sv[NW][U][CPR], zv[NW][U][CPR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int row = row0 + u * RPW + rsub;
 #pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const int wi = c * LPR * 4 + sub * 4;
-            if (row < N) {
-                wv[u][c] = *(const u32x4*)(codes + (int64_t)row * wpr + wi);
-                const int64_t sg = (int64_t)row * groups + wi / F::kWordsPerGroup;
-                sv[u][c] = scales[sg];
-                zv[u][c] = zeros[sg];
-            } else {
-                wv[u][c] = u32x4{0, 0, 0, 0};
-                sv[u][c] = 0;
-                zv[u][c] = 0;
+        for (int b = 0; b < NW; ++b)
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) {
+                const int wi = c * LPR * 4 + sub * 4;
+                if (row < N) {
+                    wv[b][u][c] = *(const u32x4*)(W.codes[b] + (int64_t)row * wpr + wi);
+                    const int64_t sg = (int64_t)row * groups + wi / F::kWordsPerGroup;
+                    sv[b][u][c] = W.scales[b][sg];
+                    zv[b][u][c] = W.zeros[b][sg];
+                } else {
+                    wv[b][u][c] = u32x4{0, 0, 0, 0};
+                    sv[b][u][c] = 0;
+                    zv[b][u][c] = 0;
+                }
             }
-        }
     }
 
     // Activations for this lane's k positions, reused for every row.
@@ -223,19 +236,31 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        float acc = 0.0f;
+        float acc[NW];
 #pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            float a[G::NC];
+        for (int b = 0; b < NW; ++b) {
+            acc[b] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
-            G::accumulate(wv[u][c], xr[c], a);
-            const float t = G::centred(a, xs[c], xs_all[c], (float)as_f16(zv[u][c]));
-            acc += t * (float)as_f16(sv[u][c]);
+            for (int c = 0; c < CPR; ++c) {
+                float a[G::NC];
+#pragma unroll
+                for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
+                G::accumulate(wv[b][u][c], xr[c], a);
+                const float t = G::centred(a, xs[c], xs_all[c], (float)as_f16(zv[b][u][c]));
+                acc[b] += t * (float)as_f16(sv[b][u][c]);
+            }
+            acc[b] = segment_sum<LPR>(acc[b]);
         }
-        acc = segment_sum<LPR>(acc);
         const int row = row0 + u * RPW + rsub;
-        if (sub == 0 && row < N) epi_store(out, 0, row, acc);
+        if (sub == 0 && row < N) {
+            if constexpr (NW == 1) {
+                epi_store(out, 0, row, acc[0]);
+            } else {
+                const uint16_t g16 = f32_to_f16_bits(acc[0]);
+                gout[row] = g16;
+                out.Y[row] = swiglu_f16(g16, f32_to_f16_bits(acc[1]));
+            }
+        }
     }
 }
 
@@ -416,17 +441,21 @@ GemvShape gemv_shape(int bits, int K) {
 // registers (and the fused LayerNorm) but cut the number of waves in flight.
 // Measured on MI355X with the loop block's weights cache-resident: U = 4 from
 // 8192 row steps (FFN up), U = 2 from 2048 (QKV, out, down), else U = 1; at
-// most 8 outstanding 16-byte code loads per lane (U * CPR <= 8).
-template <int BITS, int LPR, int CPR, int U, bool LN>
+// most 8 outstanding 16-byte code loads per lane (U * CPR * NW <= 8, NW = 2
+// for the SwiGLU pair).
+template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
 hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
+    static_assert(U * CPR * NW <= 8, "at most 8 code loads per lane");
     constexpr int RPW = 64 / LPR;
     constexpr int kWavesPerBlock = 4;
     const int N = a.w->N;
     const int steps = (N + RPW - 1) / RPW;
     const int waves = (steps + U - 1) / U;
     const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    k_gemv<BITS, LPR, CPR, U, LN><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
-        a.X, a.ln_h, a.norm_out, a.w->codes, a.w->scales, a.w->zeros, N, a.out());
+    const qg_weight* w1 = NW == 2 ? a.w2 : a.w;
+    const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros}};
+    k_gemv<BITS, LPR, CPR, U, LN, NW><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
+        a.X, a.ln_h, a.norm_out, W, N, a.out(), a.g_out);
     return hipGetLastError();
 }
 
@@ -445,13 +474,26 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
     } else {
     constexpr int RPW = 64 / LPR;
     const int steps = (a.w->N + RPW - 1) / RPW;
+    if (a.w2 != nullptr) {  // SwiGLU pair: two weights per row step
+        if constexpr (CPR <= 4) {
+            if constexpr (CPR == 1) {
+                if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN, 2>(a, s);
+            }
+            if constexpr (CPR <= 2) {
+                if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 2>(a, s);
+            }
+            return launch_gemv_u<BITS, LPR, CPR, 1, LN, 2>(a, s);
+        } else {
+            return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_swiglu
+        }
+    }
     if constexpr (CPR <= 2) {
-        if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN>(a, s);
+        if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN, 1>(a, s);
     }
     if constexpr (CPR <= 4) {
-        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN>(a, s);
+        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 1>(a, s);
     }
-    return launch_gemv_u<BITS, LPR, CPR, 1, LN>(a, s);
+    return launch_gemv_u<BITS, LPR, CPR, 1, LN, 1>(a, s);
     }
 }
 
@@ -505,6 +547,10 @@ bool gemm_fuses_layernorm(int bits, int M, int K, int N) {
     return gemm_path(bits, M, K, N) == kPathGemv && K % 1024 == 0 && K <= 8192;
 }
 
+bool gemm_fuses_swiglu(int bits, int M, int K, int N) {
+    return gemm_path(bits, M, K, N) == kPathGemv && gemv_shape(bits, K).cpr <= 4;
+}
+
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {
     switch (gemm_path(bits, M, K, N)) {
         case kPathSkinny: {
@@ -518,6 +564,9 @@ size_t gemm_ws_bytes(int bits, int M, int K, int N) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int bits = a.w->bits;
+    if (a.w2 != nullptr && !(gemm_fuses_swiglu(bits, a.M, a.w->K, a.w->N) && a.epi == kStore &&
+                             a.w2->bits == bits && a.w2->K == a.w->K && a.w2->N == a.w->N))
+        return hipErrorInvalidValue;
     switch (gemm_path(bits, a.M, a.w->K, a.w->N)) {
         case kPathGemv: return bits == 4 ? launch_gemv<4>(a, s) : launch_gemv<2>(a, s);
         case kPathSkinny: return bits == 4 ? launch_skinny<4>(a, s) : launch_skinny<2>(a, s);

@@ -150,9 +150,17 @@ int check_block(const qg_block* b, const char* fn) {
     return QG_OK;
 }
 
+// QG_FUSE_SWIGLU=0 keeps the gate and up projections of a gated block as two
+// launches even where one SwiGLU pair launch could run them (the fused-versus-
+// separate parity test); read on every call.
+bool swiglu_fusion_enabled() {
+    const char* v = getenv("QG_FUSE_SWIGLU");
+    return !(v && v[0] == '0');
+}
+
 // Enqueue `iters` iterations of the loop block on stream s (no validation).
 hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
-                        const LoopLayout& L, hipStream_t s) {
+                        const LoopLayout& L, bool fuse_swiglu, hipStream_t s) {
     char* base = (char*)scratch;
     qg_half* norm = (qg_half*)(base + L.norm);
     qg_half* qkv = (qg_half*)(base + L.qkv);
@@ -167,6 +175,9 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     qg_half* g = gate ? (qg_half*)(base + L.g) : nullptr;
     const bool fuse_qkv = qg::gemm_fuses_layernorm(blk->qkv.bits, M, D, 3 * D);
     const bool fuse_first = qg::gemm_fuses_layernorm(gate ? blk->gate.bits : blk->up.bits, M, D, F);
+    // At M == 1 a gated block runs gate and up as one SwiGLU pair launch.
+    const bool pair = gate && fuse_swiglu && blk->gate.bits == blk->up.bits &&
+                      qg::gemm_fuses_swiglu(blk->up.bits, M, D, F);
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
         qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
         if (fuse_qkv)
@@ -190,8 +201,13 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
         } else if (e == hipSuccess) {
             e = qg::launch_layernorm(h, M, D, norm, s);
         }
+        if (pair) {
+            fa.w2 = &blk->up;
+            fa.g_out = g;
+            fa.Y = u;
+        }
         if (e == hipSuccess) e = qg::launch_gemm(fa, s);
-        if (gate && e == hipSuccess) {
+        if (gate && !pair && e == hipSuccess) {
             qg::GemmArgs ua{norm, D, &blk->up, u, F, M, qg::kGateMul, nullptr, 0, ws, L.ws_bytes};
             ua.gm = g;
             ua.ldg = F;
@@ -218,6 +234,7 @@ struct LoopKey {
     const float* h;
     void* scratch;
     int32_t M, iters, device;
+    bool fuse_swiglu;
     bool operator==(const LoopKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
 };
 
@@ -234,7 +251,7 @@ hipStream_t g_capture_stream[64] = {nullptr};
 constexpr size_t kMaxGraphs = 32;
 
 hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
-                      const LoopLayout& L, hipGraphExec_t* out) {
+                      const LoopLayout& L, bool fuse_swiglu, hipGraphExec_t* out) {
     LoopKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
     key.blk = *blk;
@@ -242,6 +259,7 @@ hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, v
     key.scratch = scratch;
     key.M = M;
     key.iters = iters;
+    key.fuse_swiglu = fuse_swiglu;
     hipError_t e = hipGetDevice(&key.device);
     if (e != hipSuccess) return e;
     if (key.device < 0 || key.device >= 64) return hipErrorInvalidDevice;
@@ -259,7 +277,7 @@ hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, v
         return e;
     }
     if ((e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
-    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, cs);
+    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {
@@ -480,11 +498,12 @@ int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t 
     // Inside a caller's graph capture, or with graphs switched off, the
     // kernels are enqueued one by one; otherwise the iteration sequence is
     // replayed from a cached graph (one launch instead of 4-6 per iteration).
+    const bool fuse_swiglu = swiglu_fusion_enabled();
     if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled()) {
-        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, s);
+        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, s);
     } else {
         hipGraphExec_t exec = nullptr;
-        e = loop_graph(blk, h, M, L1 - L0, scratch, L, &exec);
+        e = loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, &exec);
         if (e == hipSuccess) e = hipGraphLaunch(exec, s);
     }
     if (e != hipSuccess) return hip_fail(fn, e);

@@ -179,8 +179,11 @@ def test_loop_inside_caller_graph_capture(orc):
 # epilogue -- GEMV (M=1), skinny (M=3, 16), staged tiled (M=33), ring (M=300),
 # and the split reduction (D=4096: skinny K parts at M=5, tiled K split at
 # M=20).
+# M = 1 at D = 512 (no fused LayerNorm), 4096 and 8192 runs the
+# gate and up projections as one SwiGLU pair launch (1, 2 and 4 lane chunks
+# per row for INT4).
 GATED = [(1, 256, 640), (3, 256, 640), (16, 256, 640), (33, 256, 640), (300, 2048, 8192),
-         (5, 4096, 256), (20, 4096, 256)]
+         (5, 4096, 256), (20, 4096, 256), (1, 512, 1152), (1, 4096, 384), (1, 8192, 128)]
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -232,3 +235,45 @@ def test_loop_gated_graph_replays_match_direct_enqueue(orc, monkeypatch):
         monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
         qg.qg_loop_range(blk, h0.clone(), 0, 1, scratch)
         torch.cuda.synchronize()
+
+
+# The SwiGLU pair launch (gate and up in one M = 1 GEMV) computes exactly what
+# the separate gate GEMV and gate-multiply up GEMV compute: same lanes, same
+# reduction order, same FP32 silu.  INT2 at D = 512 has no GEMV shape, so it
+# stays on the separate path on both sides.
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("D,F", [(512, 1152), (1024, 2944), (2048, 8192), (4096, 384),
+                                 (8192, 128)])
+def test_loop_swiglu_pair_matches_separate_launches(orc, monkeypatch, bits, D, F):
+    M, L = 1, 3
+    inp, blk, _ = _blocks(orc, M, bits, D, F, seed=D + F, gated=True)
+    h0 = inp.X.float().cuda()
+    out = {}
+    for fuse in ("1", "0"):
+        monkeypatch.setenv("QG_FUSE_SWIGLU", fuse)
+        h = h0.clone()
+        scratch = qg.alloc_loop_scratch(blk, M)
+        qg.qg_loop_range(blk, h, 0, L, scratch)
+        torch.cuda.synchronize()
+        v = qg.scratch_views(blk, M, scratch)
+        out[fuse] = (h.cpu(), v["g"].cpu(), v["u"].cpu(), v["norm"].cpu())
+    for name, a, b in zip(("h", "g", "u", "norm"), out["1"], out["0"]):
+        assert torch.equal(a, b), f"bits={bits} D={D} F={F}: {name} differs between the pair " \
+                                  f"launch and the separate launches"
+
+
+def test_loop_gated_mixed_bits_block(orc):
+    """A gate in INT4 with the rest in INT2 (not a SwiGLU pair: the bits
+    differ) at M = 1, against the oracle."""
+    D, F, M, L = 2048, 1024, 1, 2
+    inp = workloads.block(M, seed=5, D=D, F=F, gated=True)
+    ws = {k: qg.qg_pack(v.cuda(), 4 if k == "gate" else 2) for k, v in inp.W.items()}
+    blk = qg.Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws["gate"])
+    ow = {k: orc.pack(v.numpy(), 4 if k == "gate" else 2) for k, v in inp.W.items()}
+    oblk = orc.Block(D, F, ow["qkv"], ow["out"], ow["up"], ow["down"], ow["gate"])
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    href, last = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
+    _check_h(h.cpu().numpy(), href, "mixed-bits gated h")
+    _check_scratch(qg.scratch_views(blk, M, scratch), last, slice(None), "mixed-bits gated")
