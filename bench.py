@@ -281,6 +281,8 @@ def extra_legs(qg, torch, workloads, args):
     loop_case("c4a_int2_block_m1_l16", 2, 1, 16)
     loop_case("c4b_int2_block_m128_l8", 2, 128, 8)
     loop_case("c5a_int4_block_m16_l32", 4, 16, 32)
+    # Medium M (batched decode between the skinny and the 128-row tiles).
+    loop_case("next3_int4_block_m64_l8", 4, 64, 8)
     # SwiGLU block (gate projection D x F added): decode and prefill.
     loop_case("next2_int4_gated_block_m1_l8", 4, 1, 8, gated=True)
     loop_case("next2_int4_gated_block_m512_l8", 4, 512, 8, gated=True)

@@ -309,7 +309,8 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
 //      codes of one group; chunk q of column n at unit CH n + (q ^ swz(n)),
 //      again so that 16 consecutive columns read distinct banks.
 // Scales and zeros come 8 groups at a time (16 contiguous bytes per column)
-// into a double buffer.
+// into a double buffer; a K part of at most 8 groups (SZR) instead holds its
+// column's scales and zeros in registers, loaded once before the first step.
 //
 // The four waves each own a 32-column strip of the 128-wide tile (TM = BM/32
 // MFMA tiles of 32 x 32 down it), so a wave dequantises each B fragment once
@@ -327,11 +328,12 @@ struct RingB {
     __device__ static int swz(int n) { return BITS == 4 ? (n >> 2) & 3 : (n >> 3) & 1; }
 };
 
-// The ring kernel needs 16-byte aligned DMA sources and runs of 8 groups of
-// scales that stay inside one K part.
+// The ring kernel needs 16-byte aligned DMA sources, and K parts of whole
+// runs of 8 groups of scales (DMA) or of at most 8 groups (registers).
 bool ring_ok(const GemmArgs& a, int split) {
     const int groups = a.w->K / kBK;
-    return groups % split == 0 && (groups / split) % 8 == 0 && (a.ldx % 8) == 0 &&
+    const int per = groups / split;
+    return groups % split == 0 && (per % 8 == 0 || per <= 8) && (a.ldx % 8) == 0 &&
            ((uintptr_t)a.X % 16) == 0 && ((uintptr_t)a.w->codes % 16) == 0 &&
            ((uintptr_t)a.w->scales % 16) == 0 && ((uintptr_t)a.w->zeros % 16) == 0;
 }
@@ -382,7 +384,7 @@ __device__ __forceinline__ void for_each_index(Fn&& f, std::integer_sequence<int
     (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int BITS, int BM, int RA, int RBS>
+template <int BITS, int BM, int RA, int RBS, bool SZR>
 __global__ __launch_bounds__(256) void k_gemm_ring(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
@@ -439,6 +441,17 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         b_off[i] = (uint32_t)(n * wpr * 4 + g_lo * F::kWordsPerGroup * 4 + q * 16);
     }
     const uint32_t sz_off = (uint32_t)((((wave & 1) * 64 + lane) * groups + g_lo) * 2);
+    // SZR: this lane's column's scales and zeros of the part (G <= 8 groups).
+    uint16_t sreg[8], zreg[8];
+    if constexpr (SZR) {
+        const int n = n0 + wave * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool ok = i < G && n < N;
+            sreg[i] = ok ? scales[(int64_t)n * groups + g_lo + i] : (uint16_t)0;
+            zreg[i] = ok ? zeros[(int64_t)n * groups + g_lo + i] : (uint16_t)0;
+        }
+    }
 
     // Iteration t issues A of step t + RA - 1, then B (and, every 8 steps,
     // the scales and zeros of the next 8) of step t + RB - 1.
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
 #pragma unroll
             for (int i = 0; i < B_DMA; ++i)
                 dma16(rb, dst + i * 1024, b_off[i] + sb * F::kWordsPerGroup * 4);
-            if ((sb & 7) == 0)
+            if (!SZR && (sb & 7) == 0)
                 dma16(rsz, &lds_sz[(sb >> 3) & 1][wave >> 1][(wave & 1) * 1024], sz_off + sb * 2);
         }
     };
@@ -486,9 +499,14 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         constexpr int SB = decltype(sb_c)::value;
         const uint8_t* As = lds_a[SA];
         const uint8_t* Bs = lds_b[SB];
-        const uint8_t* Sz = &lds_sz[(step >> 3) & 1][0][(step & 7) * 2];
-        const GroupConst gc = group_const(*(const uint16_t*)(Sz + sz_lds),
-                                          *(const uint16_t*)(Sz + 128 * 16 + sz_lds));
+        GroupConst gc;
+        if constexpr (SZR) {
+            gc = group_const(sreg[step & 7], zreg[step & 7]);
+        } else {
+            const uint8_t* Sz = &lds_sz[(step >> 3) & 1][0][(step & 7) * 2];
+            gc = group_const(*(const uint16_t*)(Sz + sz_lds),
+                             *(const uint16_t*)(Sz + 128 * 16 + sz_lds));
+        }
         uint32_t wd[LANE_WORDS];
 #pragma unroll
         for (int v = 0; v < LANE_WORDS / 4; ++v) {
@@ -544,7 +562,11 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     };
 
     for (int t = -(RBS - 1); t < 0; ++t) issue(t);
-    for (int g0 = 0; g0 < G; g0 += U) {
+    // (SZR: a fixed, fully unrolled trip count, so that the register arrays
+    // are indexed by constants)
+    constexpr int G_UNROLL = SZR ? (8 + U - 1) / U * U : 0;
+#pragma unroll
+    for (int g0 = 0; g0 < (SZR ? G_UNROLL : G); g0 += U) {
         // steps g0 .. g0 + U - 1 with compile-time stage indices (g0 % U == 0)
         for_each_index([&](auto u_c) {
             constexpr int u = decltype(u_c)::value;
@@ -594,32 +616,66 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 struct Plan {
-    int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64, 3: ring 128x128
+    int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64, 3: ring 128x128,
+                // 4: ring 32x128
     int split;  // K parts
 };
 
+// Up to this M the ring kernel runs 32-row tiles.
+constexpr int kMidMaxM = 256;
+
+// Ring kernel with 32-row tiles: K split into the most parts (at most 8) that
+// keep at most 256 workgroups and at least 8 groups per part; {-1, 0} where
+// the parts would not suit the ring.
+Plan plan_ring32(int M, int N, int groups) {
+    const int t32 = ceil_div(M, 32) * ceil_div(N, 128);
+    int sp = 1;
+    while (2 * sp <= 8 && t32 * 2 * sp <= 256 && groups % (2 * sp) == 0 && groups / (2 * sp) >= 8)
+        sp *= 2;
+    const int per = groups / sp;
+    if (groups % sp == 0 && (per % 8 == 0 || per <= 8)) return {4, sp};
+    return {-1, 0};
+}
+
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Tile choice, from sweeps on MI355X over the block shapes and M = 32..2048.
-// The ring kernel (one workgroup per CU, operands prefetched by LDS DMA)
-// wins from about 192 128x128 tiles up to about 1024, and with K split into
-// parts of at least 8 groups when K >= 4096 gives too few tiles; it needs
-// aligned operands (ring = false otherwise).  Past 1024 tiles, single-stage
-// 128x128 workgroups (two resident per CU overlap each other's barriers);
-// with about one tile per CU, 128x128 on eight waves splitting each step's
-// k-slices in two; with fewer tiles, 64x64 workgroups of four 32x32 waves,
-// several resident per CU, K split over up to 8 parts of at least 4 groups.
+// Tile choice, from sweeps on MI355X over the block's four shapes, INT4 and
+// INT2, M = 17..2048.  The ring kernels (operands prefetched by LDS DMA) need
+// aligned operands (ring = false otherwise):
+//   * M <= kMidMaxM (batched decode): 32-row ring tiles (plan_ring32).  More,
+//     smaller tiles beat fewer 128-row ones here although each 32-row tile
+//     dequantises its B tile again: these launches are bound by per-step
+//     latency and by how many CUs have work, not by the dequantisation
+//     (0-30 % faster than the best other tile at M = 17..256);
+//   * 128-row ring tiles from 192 tiles up to 2048 (measured to 1024), and
+//     with K split into parts of at least 8 groups where K >= 4096 leaves too
+//     few tiles;
+//   * other shapes with fewer than 192 128-row tiles: 32-row ring tiles again
+//     (up to 30 % faster than the staged kernels at M = 384..1024).
+// Otherwise the staged kernels: past 2048 tiles single-stage 128x128
+// workgroups (two resident per CU overlap each other's barriers); with about
+// one tile per CU, 128x128 on eight waves splitting each step's k-slices in
+// two; with fewer tiles, 64x64 workgroups of four 32x32 waves, several
+// resident per CU, K split over up to 8 parts of at least 4 groups.
 Plan plan_for(int M, int N, int K, bool ring) {
     const int groups = K / kBK;
     const int t128 = ceil_div(M, 128) * ceil_div(N, 128);
     const int t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    if (ring && M <= kMidMaxM) {
+        const Plan p = plan_ring32(M, N, groups);
+        if (p.cfg >= 0) return p;
+    }
     if (ring && groups % 8 == 0) {
-        if (t128 >= 192 && t128 < 1024) return {3, 1};
+        if (t128 >= 192 && t128 < 2048) return {3, 1};
         if (t128 < 192 && groups >= 32) {
             int sp = 1;
             while (sp < 8 && t128 * sp < 192) sp *= 2;
             if (t128 * sp >= 192 && (groups / sp) % 8 == 0) return {3, sp};
         }
+    }
+    if (ring && t128 < 192) {
+        const Plan p = plan_ring32(M, N, groups);
+        if (p.cfg >= 0) return p;
     }
     if (t128 >= 512) return {0, 1};
     if (t128 >= 240) return {1, 1};
@@ -652,7 +708,7 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     return reduce_parts(a, split, part, s);
 }
 
-template <int BITS, int BM, int RA, int RBS>
+template <int BITS, int BM, int RA, int RBS, bool SZR>
 hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const int gx = (a.w->N + 127) / 128, gy = (a.M + BM - 1) / BM;
     const double a_bytes = (double)BM * a.w->K * 2 / split;
@@ -660,7 +716,7 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const Raster rs = make_raster(gx, gy, a_bytes, b_bytes);
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
     float* part = split > 1 ? (float*)a.ws : nullptr;
-    k_gemm_ring<BITS, BM, RA, RBS><<<grid, 256, 0, s>>>(
+    k_gemm_ring<BITS, BM, RA, RBS, SZR><<<grid, 256, 0, s>>>(
         a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
         a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
@@ -671,12 +727,19 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
 template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
     Plan p = plan_for(a.M, a.w->N, a.w->K, true);
-    if (p.cfg == 3 && !ring_ok(a, p.split)) p = plan_for(a.M, a.w->N, a.w->K, false);
+    if (p.cfg >= 3 && !ring_ok(a, p.split)) p = plan_for(a.M, a.w->N, a.w->K, false);
+    // scales and zeros from registers where the part is not whole runs of 8
+    const bool szr = (a.w->K / kBK / p.split) % 8 != 0;
     switch (p.cfg) {
         case 0: return launch_cfg<BITS, 128, 128, 2, 2, 1, 1, 0>(a, p.split, s);
         case 1: return launch_cfg<BITS, 128, 128, 2, 2, 2, 2, 2>(a, p.split, s);
         case 2: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
-        default: return launch_ring<BITS, 128, 2, 4>(a, p.split, s);
+        case 3:
+            return szr ? launch_ring<BITS, 128, 2, 4, true>(a, p.split, s)
+                       : launch_ring<BITS, 128, 2, 4, false>(a, p.split, s);
+        default:
+            return szr ? launch_ring<BITS, 32, 2, 4, true>(a, p.split, s)
+                       : launch_ring<BITS, 32, 2, 4, false>(a, p.split, s);
     }
 }
 

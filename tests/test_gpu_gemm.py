@@ -86,11 +86,11 @@ def test_gemm_long_prefill_down_proj_sampled_rows(orc):
     assert np.all(np.isfinite(Y))
 
 
-# Shapes whose tile plan runs the LDS-DMA ring kernel: >= 192 output tiles of
-# 128 x 128 (ragged M and N edges), and K = 8192 with too few tiles, split
-# into 8 parts of 8 groups.  Rows are independent, so the oracle checks rows
-# at both edges of every 128-row block.
-RING_CASES = [(300, 2048, 8200), (130, 8192, 1500), (1024, 2048, 6144)]
+# Shapes whose tile plan runs the LDS-DMA ring kernel with 128-row tiles:
+# >= 192 output tiles of 128 x 128 (ragged M and N edges), and K = 8192 with
+# too few tiles, split into 8 parts of 8 groups.  Rows are independent, so the
+# oracle checks rows at both edges of every 128-row block.
+RING_CASES = [(300, 2048, 8200), (520, 8192, 1000), (1024, 2048, 6144)]
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -116,6 +116,34 @@ def test_gemm_ring_path_sampled_rows(orc, bits, M, K, N):
     Y = g.view.float().cpu().numpy()
     rows = sorted({r for b in range(0, M, 128) for r in (b, min(b + 127, M - 1))} | {M - 1})
     assert_close(Y[rows], orc.gemm(X.numpy()[rows], op), f"ring bits={bits} M={M} K={K} N={N}")
+
+
+# Shapes whose tile plan runs the ring kernel with 32-row tiles: M <= 256
+# (batched decode) and larger M with few 128-row tiles.  Scales and zeros come
+# by DMA for parts of whole runs of 8 groups, from registers for K of 3, 5 and
+# 7 groups; K split into 2 and 8 parts.  The last case is 1024 128-row tiles,
+# the 128-row ring's largest measured size.
+RING32_CASES = [(40, 1024, 1000), (17, 640, 300), (100, 384, 520), (33, 2048, 6144),
+                (64, 8192, 2048), (200, 8192, 1500), (384, 2048, 2048), (700, 896, 700),
+                (2048, 2048, 8192)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", RING32_CASES)
+def test_gemm_ring32_paths(orc, bits, M, K, N):
+    W, X = workloads.single_gemm(M, K, N, seed=M + K + N + bits)
+    p = qg.qg_pack(W.cuda(), bits)
+    op = orc.pack(W.numpy(), bits)
+    g = Guarded(M, N, (N + 15) // 8 * 8)
+    GEMM[bits](X.cuda(), p, Y=g.view)
+    torch.cuda.synchronize()
+    g.check()
+    Y = g.view.float().cpu().numpy()
+    blk = 32 if M <= 1024 else 128
+    rows = sorted({r for b in range(0, M, blk) for r in (b, min(b + blk - 1, M - 1))} | {M - 1})
+    if M <= 64:
+        rows = list(range(M))
+    assert_close(Y[rows], orc.gemm(X.numpy()[rows], op), f"ring32 bits={bits} M={M} K={K} N={N}")
 
 
 @pytest.mark.parametrize("offset", [0, 1])
