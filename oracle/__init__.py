@@ -142,8 +142,8 @@ def halves_to_double(bits) -> np.ndarray:
 
 @dataclass
 class Packed:
-    """One packed weight: codes [N][K*bits/32] uint32, scales/zeros [N][K/128]
-    FP16 bit patterns (uint16)."""
+    """One packed weight: codes [N][K*bits/32] uint32, scales/zeros [N][K/group]
+    FP16 bit patterns (uint16); group 128, or K for per-row groups."""
     bits: int
     K: int
     N: int
@@ -239,10 +239,14 @@ class Block:
                       self.down.cstruct(), gate)
 
 
-def pack_block(W: dict, bits: int, D: int, F: int) -> Block:
-    """Pack qkv, out, up, down (and gate, when W has one)."""
-    ws = {k: pack(np.asarray(W[k]), bits) for k in ("qkv", "out", "up", "down")}
-    gate = pack(np.asarray(W["gate"]), bits) if "gate" in W else None
+def pack_block(W: dict, bits: int, D: int, F: int, per_row: bool = False) -> Block:
+    """Pack qkv, out, up, down (and gate, when W has one); per_row: one group
+    per output channel (group = K) instead of groups of 128."""
+    def p(k):
+        a = np.asarray(W[k])
+        return pack(a, bits, a.shape[0] if per_row else GROUP)
+    ws = {k: p(k) for k in ("qkv", "out", "up", "down")}
+    gate = p("gate") if "gate" in W else None
     return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], gate)
 
 

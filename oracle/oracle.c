@@ -14,7 +14,9 @@
  *  - "β-Informed Deployment Features" page, CTX-TIER "Details of the shipped
  *    kernel": per-group asymmetric quantisation, groups of typically 128
  *    weights, INT2 scale = (max - min) / 3, four INT2 codes per byte, a row of
- *    codes is one output channel (INT4 row stride K/2 bytes, INT2 K/4 bytes).
+ *    codes is one output channel (INT4 row stride K/2 bytes, INT2 K/4 bytes);
+ *    Phase 2b also meets per-row quantisation, one group spanning the whole
+ *    row (group size = K).
  *  - "Warm-start mid-loop" page, internal flow: run_loop_iters_range applies
  *    iterations [L_used, new_L) in place on the residual; the shared block
  *    re-applies the same weights on every iteration.
@@ -29,6 +31,8 @@
  *    16*(j mod 2) + b*floor(j/2): the even codes fill the low 16 bits and the
  *    odd codes the high 16 bits, each half from its least significant bit;
  *  - layout: codes [N][K*b/32] uint32, scales/zeros [N][K/G] FP16, N-major;
+ *  - group size G: 128, or K for per-row groups (one scale and zero per
+ *    output channel); K is a multiple of 128 either way;
  *  - glue between the projections: parameter-free LayerNorm (eps 1e-5,
  *    population variance), self-only attention (the V slice of qkv, columns
  *    [2D, 3D)), identity FFN activation (or SwiGLU when the block has a gate
@@ -117,9 +121,9 @@ static int check_format(int32_t bits, int32_t K, int32_t N, int32_t group)
 {
     if (bits != 2 && bits != 4)
         return OR_EUNSUPPORTED;
-    if (group != 128)
+    if (group != 128 && group != K)
         return OR_EUNSUPPORTED;
-    if (K <= 0 || N <= 0 || K % group != 0)
+    if (K <= 0 || N <= 0 || K % 128 != 0)
         return OR_EINVAL;
     return OR_OK;
 }
