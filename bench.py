@@ -235,9 +235,9 @@ def extra_legs(qg, torch, workloads, args):
     del pool
     sync()
 
-    def loop_case(name, bits, M, L, gated=False):
+    def loop_case(name, bits, M, L, gated=False, per_row=False):
         inp = workloads.block(M, seed=0, gated=gated)
-        blk = qg.pack_block(inp.W, bits, D, F)
+        blk = qg.pack_block(inp.W, bits, D, F, per_row=per_row)
         scratch = qg.alloc_loop_scratch(blk, M)
         h = inp.X.float().to(dev)
         t1 = time_loop(qg, torch, blk, h, L, scratch, 1, 2)
@@ -248,6 +248,8 @@ def extra_legs(qg, torch, workloads, args):
              "TFLOP/s": round(block_flops(M, gated=gated) * L / per / 1e12, 2)}
         if gated:
             r["ffn"] = "swiglu"
+        if per_row:
+            r["group"] = "per-row (K)"
         r["frac_hbm"] = round(r["eff_weight_GB/s"] / HBM_PEAK_GBS, 4)
         r["frac_mfma"] = round(r["TFLOP/s"] / MFMA_F16_PEAK_TFLOPS, 4)
         out[name] = r
@@ -283,6 +285,8 @@ def extra_legs(qg, torch, workloads, args):
     loop_case("c5a_int4_block_m16_l32", 4, 16, 32)
     # Medium M (batched decode between the skinny and the 128-row tiles).
     loop_case("next3_int4_block_m64_l8", 4, 64, 8)
+    # Per-row groups (one scale and zero per output channel): decode.
+    loop_case("next3_int4_perrow_block_m1_l8", 4, 1, 8, per_row=True)
     # SwiGLU block (gate projection D x F added): decode and prefill.
     loop_case("next2_int4_gated_block_m1_l8", 4, 1, 8, gated=True)
     loop_case("next2_int4_gated_block_m512_l8", 4, 512, 8, gated=True)

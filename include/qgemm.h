@@ -7,9 +7,11 @@
  * "β-Informed Deployment Features" page, CTX-TIER section): FP16 activations
  * times INT4- or INT2-packed weights that carry one FP16 scale and one FP16
  * zero per group of 128 weights along K ("Model" page, VRAM cost; CTX-TIER
- * "Details of the shipped kernel").
+ * "Details of the shipped kernel"), or per row: one group spanning all of K
+ * (CTX-TIER Phase 2b meets such per-row weights, group size = K).
  *
- * Packed format, layout version 1 (b = bits in {4, 2}, G = 128, g = k / G):
+ * Packed format, layout version 1 (b = bits in {4, 2}, G = group = 128 or K,
+ * g = k / G):
  *   - codes:  uint32 [N][K*b/32], row n = output channel n, contiguous along K
  *             (INT4 rows are K/2 bytes, INT2 rows K/4 bytes).  Inside a word,
  *             code j (j = k mod 32/b) sits at bit 16*(j mod 2) + b*floor(j/2):
@@ -62,8 +64,9 @@ extern "C" {
 typedef uint16_t qg_half; /* IEEE binary16 bit pattern */
 
 /* One packed weight (the pages' QuantWeight: packed data, FP16 scales and
- * zeros, bits; CTX-TIER Phase 2).  bits in {4, 2}; group == 128; K % 128 == 0;
- * N >= 1; codes 16-byte aligned; scales/zeros 2-byte aligned. */
+ * zeros, bits; CTX-TIER Phase 2).  bits in {4, 2}; group == 128 or group == K
+ * (per-row: scales and zeros are [N][1]); K % 128 == 0; N >= 1; codes 16-byte
+ * aligned; scales/zeros 2-byte aligned. */
 typedef struct qg_weight {
     int32_t bits;
     int32_t K;
@@ -74,10 +77,8 @@ typedef struct qg_weight {
     const qg_half* zeros;
 } qg_weight;
 
-/* The loop block's four projections (CTX-TIER Phase 2b names the block's
- * attn_qkv, attn_out, mlp_up and mlp_down weights): qkv K=D, N=3D; out K=D,
- * N=D; up K=D, N=F; down K=F, N=D.  Each weight carries its own bits. */
-/* The looped block's weights.  gate.codes == NULL (all of gate zero): four
+/* The looped block's weights: qkv K=D, N=3D; out K=D, N=D; up K=D, N=F;
+ * down K=F, N=D.  gate.codes == NULL (all of gate zero): four
  * projections and the identity FFN activation.  Otherwise gate is the fifth
  * weight of the pages' block (mlp_gate; "β-Informed Deployment Features"
  * page, CTX-TIER Phase 2 lists attn_qkv, attn_out, mlp_gate, mlp_up,
@@ -85,7 +86,7 @@ typedef struct qg_weight {
  * ("Model" page, Parameters: ffn_dim is the width of the gate and up
  * projections): a = fp16(silu(g) * u), g = fp16(x . Wgate),
  * u = fp16(x . Wup), silu(z) = z / (1 + e^-z) evaluated in FP32.  Each weight
- * carries its own bits. */
+ * carries its own bits and group. */
 typedef struct qg_block {
     int32_t D;
     int32_t F;
@@ -103,7 +104,8 @@ const char* qg_last_error(void);
 
 /* Quantise FP32 W [K][ldw] (ldw >= N) into layout v1 (see the format above;
  * CTX-TIER kernel details: per-group asymmetric scale = range / (levels - 1)).
- * codes [N][K*bits/32], scales and zeros [N][K/128] are written in full.
+ * group: 128, or K for per-row groups (QG_EUNSUPPORTED otherwise).
+ * codes [N][K*bits/32], scales and zeros [N][K/group] are written in full.
  * Bit-identical to the definition (FP64 arithmetic on the device).
  * Synchronises `stream` before returning, because it reports non-finite W or
  * a scale that overflows FP16 as QG_EINVAL (outputs are then unspecified). */
@@ -115,8 +117,9 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
  * quantised again to INT2 with a new scale and zero).  Every group's exact
  * INT4 dequant (q - z) s goes through qg_pack's quantiser with bits = 2; the
  * result is bit-identical to that definition.
- * w4: bits 4; w2: bits 2, same K and N; both described like any qg_weight
- * (w2's codes are compact, [N][K/16]).  Out of place, w2's buffers must not
+ * w4: bits 4; w2: bits 2, same K, N and group; both described like any
+ * qg_weight (w2's codes are compact, [N][K/16]).  Per-row groups (group == K)
+ * need K <= 32768 (QG_EUNSUPPORTED otherwise).  Out of place, w2's buffers must not
  * overlap w4's or each other.  In place: w2->codes == w4->codes writes the
  * INT2 codes compactly over the first half of the INT4 code buffer (the rest
  * is left as it was), and w2->scales == w4->scales / w2->zeros == w4->zeros

@@ -113,7 +113,8 @@ def qg_last_error() -> str:
 @dataclass
 class PackedWeight:
     """Layout-v1 packed weight: codes int32 [N][K*bits/32] (uint32 bit
-    patterns), scales/zeros float16 [N][K/128]."""
+    patterns), scales/zeros float16 [N][K/group]; group 128, or K for per-row
+    groups (one scale and zero per output channel)."""
     bits: int
     K: int
     N: int
@@ -127,11 +128,15 @@ class PackedWeight:
                        self.scales.data_ptr(), self.zeros.data_ptr())
 
     @staticmethod
-    def empty(K: int, N: int, bits: int, device="cuda") -> "PackedWeight":
+    def empty(K: int, N: int, bits: int, device="cuda", group: int = GROUP) -> "PackedWeight":
+        if group not in (GROUP, K) or K % GROUP:
+            raise ValueError(f"group = {group}: layout v1 has groups of {GROUP} or per-row "
+                             f"groups (group = K = {K}), K a multiple of {GROUP}")
         return PackedWeight(bits, K, N,
                             torch.empty((N, K * bits // 32), dtype=torch.int32, device=device),
-                            torch.empty((N, K // GROUP), dtype=torch.float16, device=device),
-                            torch.empty((N, K // GROUP), dtype=torch.float16, device=device))
+                            torch.empty((N, K // group), dtype=torch.float16, device=device),
+                            torch.empty((N, K // group), dtype=torch.float16, device=device),
+                            group)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
@@ -143,7 +148,9 @@ def qg_pack(W: torch.Tensor, bits: int, group: int = GROUP, out: PackedWeight | 
     if W.dtype != torch.float32 or W.dim() != 2 or W.stride(1) != 1:
         raise ValueError("W must be a row-major FP32 [K][N] tensor")
     K, N = W.shape
-    p = out if out is not None else PackedWeight.empty(K, N, bits, W.device)
+    if out is not None and out.group != group:
+        raise ValueError(f"out.group = {out.group} but group = {group}")
+    p = out if out is not None else PackedWeight.empty(K, N, bits, W.device, group)
     _check("qg_pack", lib.qg_pack(_dev(W, "W"), W.stride(0), K, N, bits, group, p.codes.data_ptr(),
                                   p.scales.data_ptr(), p.zeros.data_ptr(), _stream(stream)))
     return p
@@ -292,9 +299,9 @@ def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place:
         if not w4.codes.is_contiguous():
             raise ValueError("in place needs contiguous INT4 codes")
         codes = w4.codes.view(-1)[:N * (K // 16)].view(N, K // 16)
-        out = PackedWeight(2, K, N, codes, w4.scales, w4.zeros)
+        out = PackedWeight(2, K, N, codes, w4.scales, w4.zeros, w4.group)
     elif out is None:
-        out = PackedWeight.empty(K, N, 2, w4.codes.device)
+        out = PackedWeight.empty(K, N, 2, w4.codes.device, w4.group)
     c4, c2 = w4.cstruct(), out.cstruct()
     _check("qg_requant_4to2", lib.qg_requant_4to2(C.byref(c4), C.byref(c2), _stream(stream)))
     return out
@@ -311,9 +318,11 @@ def requant_block(blk: Block, in_place: bool = False, stream=None) -> Block:
     return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))
 
 
-def pack_block(W: dict, bits: int, D: int, F: int, device="cuda") -> Block:
+def pack_block(W: dict, bits: int, D: int, F: int, device="cuda", per_row: bool = False) -> Block:
     """qg_pack each FP32 [K][N] projection weight of a block (qkv, out, up,
-    down, and gate when W has one)."""
-    ws = {k: qg_pack(W[k].to(device=device, dtype=torch.float32).contiguous(), bits)
+    down, and gate when W has one); per_row: one group per output channel
+    (group = K) instead of groups of 128."""
+    ws = {k: qg_pack(W[k].to(device=device, dtype=torch.float32).contiguous(), bits,
+                     W[k].shape[0] if per_row else GROUP)
           for k in ("qkv", "out", "up", "down", "gate") if k in W}
     return Block(D, F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))

@@ -27,6 +27,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kGroup = 128;
 constexpr uint32_t kBias2 = 0x64006400u;  // FP16 1024.0 in both halves
 
+// Where the scale and zero of (output channel n, 128-k group g) sit in a
+// weight's scales and zeros: element n * srow + g * sgrp.  Groups of 128
+// have (K / 128, 1); per-row groups (group size K, one scale and zero per
+// output channel) have (1, 0).  Kernels walk K in 128-k groups either way.
+struct SzIdx {
+    int srow, sgrp;
+    __host__ __device__ int64_t at(int64_t n, int64_t g) const { return n * srow + g * sgrp; }
+};
+
 template <int BITS>
 struct Fmt {
     static_assert(BITS == 4 || BITS == 2, "layout v1 has 4- and 2-bit codes");

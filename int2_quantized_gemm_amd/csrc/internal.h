@@ -12,12 +12,21 @@
 
 namespace qg {
 
+// Scale addressing of a validated weight (group 128, or K for per-row groups).
+inline SzIdx sz_idx(const qg_weight& w) {
+    return w.group == kGroup ? SzIdx{w.K / kGroup, 1} : SzIdx{1, 0};
+}
+inline bool per_row(const qg_weight& w) { return w.group != kGroup; }
+
 // ---- pack / unpack / dequant (kernels_pack.hip)
-hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, uint32_t* codes,
-                       qg_half* scales, qg_half* zeros, int* status, hipStream_t s);
+hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status,
+                       hipStream_t s);
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s);
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
                                int* status, hipStream_t s);
+// Largest K the per-row re-quantisation holds in one workgroup's registers.
+constexpr int kRequantRowMaxK = 32768;
 hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s);
 
 // ---- GEMM (kernels_gemm.hip); the epilogue kinds are in device.h.

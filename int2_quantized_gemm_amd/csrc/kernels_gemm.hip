@@ -108,6 +108,7 @@ struct GemvWeights {
     const uint32_t* codes[2];
     const uint16_t* scales[2];
     const uint16_t* zeros[2];
+    SzIdx sz;  // scale addressing, the same for both weights
 };
 
 template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     constexpr int PAIRS = 4 * F::kPairsPerWord;  // FP16 pairs of x per lane and chunk
     constexpr int K = 4 * LPR * CPR * F::kCodesPerWord;
     constexpr int wpr = K / F::kCodesPerWord;
-    constexpr int groups = K / kGroup;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int sub = lane % LPR;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                 const int wi = c * LPR * 4 + sub * 4;
                 if (row < N) {
                     wv[b][u][c] = *(const u32x4*)(W.codes[b] + (int64_t)row * wpr + wi);
-                    const int64_t sg = (int64_t)row * groups + wi / F::kWordsPerGroup;
+                    const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
                     sv[b][u][c] = W.scales[b][sg];
                     zv[b][u][c] = W.zeros[b][sg];
                 } else {
@@ -338,8 +338,8 @@ constexpr int kSkinnyMaxK = 2048;
 template <int BITS>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N, int S,
-    OutEpi out, float* __restrict__ part) {
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz, int K,
+    int N, int S, OutEpi out, float* __restrict__ part) {
     constexpr int kMaxGpw = kSkinnyMaxK / kGroup / 4;  // groups per wave
     __shared__ __attribute__((aligned(1024))) uint8_t xs[16 * kSkinnyMaxK * 2];
     __shared__ f32x4 red[4][64];
@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         if (gi < gcnt) {
             const int g = gbeg + gi;
             lc[i].load(crow, g, c);
-            sb[i] = nvalid ? scales[(int64_t)nr * groups + g] : (uint16_t)0;
-            zb[i] = zeros[(int64_t)nr * groups + g];
+            sb[i] = nvalid ? scales[sz.at(nr, g)] : (uint16_t)0;
+            zb[i] = zeros[sz.at(nr, g)];
         }
     }
 
@@ -453,7 +453,8 @@ hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     const int waves = (steps + U - 1) / U;
     const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     const qg_weight* w1 = NW == 2 ? a.w2 : a.w;
-    const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros}};
+    const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros},
+                        sz_idx(*a.w)};
     k_gemv<BITS, LPR, CPR, U, LN, NW><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
         a.X, a.ln_h, a.norm_out, W, N, a.out(), a.g_out);
     return hipGetLastError();
@@ -528,7 +529,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((a.w->N + 15) / 16, S);
     float* part = S > 1 ? (float*)a.ws : nullptr;
     k_gemm_skinny<BITS><<<grid, 256, 0, s>>>(a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros,
-                                             a.w->K, a.w->N, S, a.out(), part);
+                                             sz_idx(*a.w), a.w->K, a.w->N, S, a.out(), part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     return launch_splitk_reduce(part, S, a, s);
@@ -565,7 +566,8 @@ size_t gemm_ws_bytes(int bits, int M, int K, int N) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int bits = a.w->bits;
     if (a.w2 != nullptr && !(gemm_fuses_swiglu(bits, a.M, a.w->K, a.w->N) && a.epi == kStore &&
-                             a.w2->bits == bits && a.w2->K == a.w->K && a.w2->N == a.w->N))
+                             a.w2->bits == bits && a.w2->K == a.w->K && a.w2->N == a.w->N &&
+                             a.w2->group == a.w->group))
         return hipErrorInvalidValue;
     switch (gemm_path(bits, a.M, a.w->K, a.w->N)) {
         case kPathGemv: return bits == 4 ? launch_gemv<4>(a, s) : launch_gemv<2>(a, s);

@@ -3,9 +3,11 @@
 //
 // Quantiser ("β-Informed Deployment Features" page, CTX-TIER "Details of the
 // shipped kernel": per-group asymmetric quantisation, scale = range / 3 for
-// INT2, i.e. range / (2^b - 1)): one thread per (output channel n, group g).
-// Threads of a wave take consecutive n, so each of the 128 reads of a group
-// (W[k][n], row-major [K][ldw]) is a coalesced 256-byte wave access.  All
+// INT2, i.e. range / (2^b - 1)): one thread per (output channel n, group g),
+// groups of gl = 128 values along K, or gl = K for per-row groups (Phase 2b
+// of the same section meets weights quantised per row).  Threads of a wave
+// take consecutive n, so each of the gl reads of a group (W[k][n], row-major
+// [K][ldw]) is a coalesced 256-byte wave access.  All
 // arithmetic is FP64 with correctly rounded division and round-half-even, so
 // the result is bit-identical to the definition.
 #include "device.h"
@@ -16,19 +18,19 @@ namespace {
 
 template <int BITS>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64_t ldw, int K,
-                                              int N, uint32_t* __restrict__ codes,
+                                              int N, int gl, uint32_t* __restrict__ codes,
                                               uint16_t* __restrict__ scales,
                                               uint16_t* __restrict__ zeros, int* status) {
     using F = Fmt<BITS>;
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     const int g = blockIdx.y;
     if (n >= N) return;
-    const int groups = K / kGroup;
-    const float* col = W + (int64_t)g * kGroup * ldw + n;
+    const int groups = K / gl;
+    const float* col = W + (int64_t)g * gl * ldw + n;
 
     double lo = 0.0, hi = 0.0;
     bool bad = false;
-    for (int k = 0; k < kGroup; ++k) {
+    for (int k = 0; k < gl; ++k) {
         const double w = (double)col[(int64_t)k * ldw];
         bad |= !isfinite(w);
         lo = w < lo ? w : lo;
@@ -47,8 +49,9 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64
     scales[(int64_t)n * groups + g] = s_store;
     zeros[(int64_t)n * groups + g] = f64_to_f16_bits(z);
 
-    uint32_t* out = codes + (int64_t)n * (K / F::kCodesPerWord) + g * F::kWordsPerGroup;
-    for (int wi = 0; wi < F::kWordsPerGroup; ++wi) {
+    const int words = gl / F::kCodesPerWord;
+    uint32_t* out = codes + (int64_t)n * (K / F::kCodesPerWord) + (int64_t)g * words;
+    for (int wi = 0; wi < words; ++wi) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < F::kCodesPerWord; ++j) {
@@ -86,15 +89,15 @@ __global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ cod
 template <int BITS, bool F16OUT>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
                                                  const uint16_t* __restrict__ scales,
-                                                 const uint16_t* __restrict__ zeros, int K,
-                                                 int64_t words, void* __restrict__ out) {
+                                                 const uint16_t* __restrict__ zeros, SzIdx sz,
+                                                 int K, int64_t words, void* __restrict__ out) {
     using F = Fmt<BITS>;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= words) return;
     const int64_t wpr = K / F::kCodesPerWord;
     const int64_t n = i / wpr;
     const int64_t g = (i % wpr) / F::kWordsPerGroup;
-    const int64_t sg = n * (K / kGroup) + g;
+    const int64_t sg = sz.at(n, g);
     const GroupConst c = group_const(scales[sg], zeros[sg]);
     const uint32_t w = codes[i];
     const int64_t k0 = i * F::kCodesPerWord;  // == n*K + (i % wpr) * codes/word
@@ -114,13 +117,14 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
 
 }  // namespace
 
-hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, uint32_t* codes,
-                       qg_half* scales, qg_half* zeros, int* status, hipStream_t s) {
-    dim3 grid((N + 255) / 256, K / kGroup);
+hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status,
+                       hipStream_t s) {
+    dim3 grid((N + 255) / 256, K / group);
     if (bits == 4)
-        k_pack<4><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<4><<<grid, 256, 0, s>>>(W, ldw, K, N, group, codes, scales, zeros, status);
     else
-        k_pack<2><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<2><<<grid, 256, 0, s>>>(W, ldw, K, N, group, codes, scales, zeros, status);
     return hipGetLastError();
 }
 
@@ -136,17 +140,18 @@ hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s) {
 
 hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s) {
     const int64_t words = (int64_t)w.N * (w.K * w.bits / 32);
+    const SzIdx sz = sz_idx(w);
     const unsigned blocks = (unsigned)((words + 255) / 256);
     if (w.bits == 4) {
         if (fp16)
-            k_dequant<4, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, w.K, words, out);
+            k_dequant<4, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
         else
-            k_dequant<4, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, w.K, words, out);
+            k_dequant<4, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
     } else {
         if (fp16)
-            k_dequant<2, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, w.K, words, out);
+            k_dequant<2, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
         else
-            k_dequant<2, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, w.K, words, out);
+            k_dequant<2, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
     }
     return hipGetLastError();
 }

@@ -76,8 +76,8 @@ template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int ST
           int STORE_FROM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefill(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    OutEpi out, int groups_per_part, float* __restrict__ part) {
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz, int K,
+    int N, OutEpi out, int groups_per_part, float* __restrict__ part) {
     using C = Cfg<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES>;
     __shared__ __attribute__((aligned(16))) f16 lds[C::LDS_HALVES];
 
@@ -90,7 +90,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     const int l32 = lane & 31, hh = lane >> 5;
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
-    const int groups = K / kBK;
     const int wpr = K / Fmt<BITS>::kCodesPerWord;
     // K split: workgroup z covers groups [g_lo, g_lo + groups_per_part) and,
     // when `part` is set, writes its FP32 partial tile to part[z][M][N].
@@ -103,9 +102,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(codes + (int64_t)n0 * wpr, (int64_t)(N - n0) * wpr * 4);
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(scales + (int64_t)n0 * groups, (int64_t)(N - n0) * groups * 2);
+        make_rsrc(scales + (int64_t)n0 * sz.srow, (int64_t)(N - n0) * sz.srow * 2);
     const __amdgpu_buffer_rsrc_t rz =
-        make_rsrc(zeros + (int64_t)n0 * groups, (int64_t)(N - n0) * groups * 2);
+        make_rsrc(zeros + (int64_t)n0 * sz.srow, (int64_t)(N - n0) * sz.srow * 2);
 
     // ---- global -> registers for step g
     u32x4 a_reg[C::A_PER_T];
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
             // every resource, so they read 0 (and are not stored).
             const bool in = ch < C::B_CHUNKS;
             const uint32_t ob = in ? (uint32_t)((row * wpr + g * C::WPG + kc * 4) * 4) : 0xFFFFFF00u;
-            const uint32_t os = in ? (uint32_t)((row * groups + g) * 2) : 0xFFFFFF00u;
+            const uint32_t os = in ? (uint32_t)(sz.at(row, g) * 2) : 0xFFFFFF00u;
             b_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0);
             s_reg[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
             z_reg[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, os, 0, 0);
@@ -308,9 +307,11 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
 //   B: 128 columns x CH chunks (CH = 4 for INT4, 2 for INT2) of the packed
 //      codes of one group; chunk q of column n at unit CH n + (q ^ swz(n)),
 //      again so that 16 consecutive columns read distinct banks.
-// Scales and zeros come 8 groups at a time (16 contiguous bytes per column)
-// into a double buffer; a K part of at most 8 groups (SZR) instead holds its
-// column's scales and zeros in registers, loaded once before the first step.
+// Scales and zeros (mode SZ) come 8 groups at a time (16 contiguous bytes per
+// column) into a double buffer (kSzDma); a K part of at most 8 groups instead
+// holds its column's scales and zeros in registers, loaded once before the
+// first step (kSzRegs); per-row groups have one scale and zero per column,
+// loaded once (kSzRow).
 //
 // The four waves each own a 32-column strip of the 128-wide tile (TM = BM/32
 // MFMA tiles of 32 x 32 down it), so a wave dequantises each B fragment once
@@ -328,14 +329,27 @@ struct RingB {
     __device__ static int swz(int n) { return BITS == 4 ? (n >> 2) & 3 : (n >> 3) & 1; }
 };
 
-// The ring kernel needs 16-byte aligned DMA sources, and K parts of whole
-// runs of 8 groups of scales (DMA) or of at most 8 groups (registers).
+enum SzMode { kSzDma = 0, kSzRegs = 1, kSzRow = 2 };
+
+// Scale mode of a ring launch over K parts of `per` groups.
+int ring_sz_mode(const GemmArgs& a, int per) {
+    return per_row(*a.w) ? kSzRow : per % 8 == 0 ? kSzDma : kSzRegs;
+}
+
+// The ring kernel needs 16-byte aligned DMA sources, and (groups of 128) K
+// parts of whole runs of 8 groups of scales (DMA) or of at most 8 groups
+// (registers).
 bool ring_ok(const GemmArgs& a, int split) {
     const int groups = a.w->K / kBK;
     const int per = groups / split;
-    return groups % split == 0 && (per % 8 == 0 || per <= 8) && (a.ldx % 8) == 0 &&
-           ((uintptr_t)a.X % 16) == 0 && ((uintptr_t)a.w->codes % 16) == 0 &&
-           ((uintptr_t)a.w->scales % 16) == 0 && ((uintptr_t)a.w->zeros % 16) == 0;
+    if (groups % split != 0 || (a.ldx % 8) != 0 || ((uintptr_t)a.X % 16) != 0 ||
+        ((uintptr_t)a.w->codes % 16) != 0)
+        return false;
+    switch (ring_sz_mode(a, per)) {
+        case kSzRow: return true;
+        case kSzRegs: return per <= 8;
+        default: return ((uintptr_t)a.w->scales % 16) == 0 && ((uintptr_t)a.w->zeros % 16) == 0;
+    }
 }
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
@@ -384,7 +398,7 @@ __device__ __forceinline__ void for_each_index(Fn&& f, std::integer_sequence<int
     (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int BITS, int BM, int RA, int RBS, bool SZR>
+template <int BITS, int BM, int RA, int RBS, int SZ>
 __global__ __launch_bounds__(256) void k_gemm_ring(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
@@ -441,9 +455,10 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         b_off[i] = (uint32_t)(n * wpr * 4 + g_lo * F::kWordsPerGroup * 4 + q * 16);
     }
     const uint32_t sz_off = (uint32_t)((((wave & 1) * 64 + lane) * groups + g_lo) * 2);
-    // SZR: this lane's column's scales and zeros of the part (G <= 8 groups).
+    // kSzRegs: this lane's column's scales and zeros of the part (G <= 8
+    // groups); kSzRow: its column's one scale and zero (groups of K).
     uint16_t sreg[8], zreg[8];
-    if constexpr (SZR) {
+    if constexpr (SZ == kSzRegs) {
         const int n = n0 + wave * 32 + l32;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -451,6 +466,11 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
             sreg[i] = ok ? scales[(int64_t)n * groups + g_lo + i] : (uint16_t)0;
             zreg[i] = ok ? zeros[(int64_t)n * groups + g_lo + i] : (uint16_t)0;
         }
+    }
+    GroupConst gc_row{};
+    if constexpr (SZ == kSzRow) {
+        const int n = n0 + wave * 32 + l32;
+        gc_row = group_const(n < N ? scales[n] : (uint16_t)0, n < N ? zeros[n] : (uint16_t)0);
     }
 
     // Iteration t issues A of step t + RA - 1, then B (and, every 8 steps,
@@ -468,7 +488,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
 #pragma unroll
             for (int i = 0; i < B_DMA; ++i)
                 dma16(rb, dst + i * 1024, b_off[i] + sb * F::kWordsPerGroup * 4);
-            if (!SZR && (sb & 7) == 0)
+            if (SZ == kSzDma && (sb & 7) == 0)
                 dma16(rsz, &lds_sz[(sb >> 3) & 1][wave >> 1][(wave & 1) * 1024], sz_off + sb * 2);
         }
     };
@@ -500,8 +520,10 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         const uint8_t* As = lds_a[SA];
         const uint8_t* Bs = lds_b[SB];
         GroupConst gc;
-        if constexpr (SZR) {
+        if constexpr (SZ == kSzRegs) {
             gc = group_const(sreg[step & 7], zreg[step & 7]);
+        } else if constexpr (SZ == kSzRow) {
+            gc = gc_row;
         } else {
             const uint8_t* Sz = &lds_sz[(step >> 3) & 1][0][(step & 7) * 2];
             gc = group_const(*(const uint16_t*)(Sz + sz_lds),
@@ -562,11 +584,12 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     };
 
     for (int t = -(RBS - 1); t < 0; ++t) issue(t);
-    // (SZR: a fixed, fully unrolled trip count, so that the register arrays
-    // are indexed by constants)
-    constexpr int G_UNROLL = SZR ? (8 + U - 1) / U * U : 0;
+    // (kSzRegs: a fixed, fully unrolled trip count, so that the register
+    // arrays are indexed by constants)
+    constexpr bool REGS = SZ == kSzRegs;
+    constexpr int G_UNROLL = REGS ? (8 + U - 1) / U * U : 0;
 #pragma unroll
-    for (int g0 = 0; g0 < (SZR ? G_UNROLL : G); g0 += U) {
+    for (int g0 = 0; g0 < (REGS ? G_UNROLL : G); g0 += U) {
         // steps g0 .. g0 + U - 1 with compile-time stage indices (g0 % U == 0)
         for_each_index([&](auto u_c) {
             constexpr int u = decltype(u_c)::value;
@@ -621,6 +644,8 @@ struct Plan {
     int split;  // K parts
 };
 
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
 // Up to this M the ring kernel runs 32-row tiles.
 constexpr int kMidMaxM = 256;
 
@@ -637,7 +662,6 @@ Plan plan_ring32(int M, int N, int groups) {
     return {-1, 0};
 }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Tile choice, from sweeps on MI355X over the block's four shapes, INT4 and
 // INT2, M = 17..2048.  The ring kernels (operands prefetched by LDS DMA) need
@@ -701,14 +725,14 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
     float* part = split > 1 ? (float*)a.ws : nullptr;
     k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
-        a.w->K / kBK / split, part);
+        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N,
+        a.out(), a.w->K / kBK / split, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || split == 1) return e;
     return reduce_parts(a, split, part, s);
 }
 
-template <int BITS, int BM, int RA, int RBS, bool SZR>
+template <int BITS, int BM, int RA, int RBS, int SZ>
 hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const int gx = (a.w->N + 127) / 128, gy = (a.M + BM - 1) / BM;
     const double a_bytes = (double)BM * a.w->K * 2 / split;
@@ -716,7 +740,7 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const Raster rs = make_raster(gx, gy, a_bytes, b_bytes);
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
     float* part = split > 1 ? (float*)a.ws : nullptr;
-    k_gemm_ring<BITS, BM, RA, RBS, SZR><<<grid, 256, 0, s>>>(
+    k_gemm_ring<BITS, BM, RA, RBS, SZ><<<grid, 256, 0, s>>>(
         a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
         a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
@@ -728,19 +752,21 @@ template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
     Plan p = plan_for(a.M, a.w->N, a.w->K, true);
     if (p.cfg >= 3 && !ring_ok(a, p.split)) p = plan_for(a.M, a.w->N, a.w->K, false);
-    // scales and zeros from registers where the part is not whole runs of 8
-    const bool szr = (a.w->K / kBK / p.split) % 8 != 0;
     switch (p.cfg) {
         case 0: return launch_cfg<BITS, 128, 128, 2, 2, 1, 1, 0>(a, p.split, s);
         case 1: return launch_cfg<BITS, 128, 128, 2, 2, 2, 2, 2>(a, p.split, s);
         case 2: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
-        case 3:
-            return szr ? launch_ring<BITS, 128, 2, 4, true>(a, p.split, s)
-                       : launch_ring<BITS, 128, 2, 4, false>(a, p.split, s);
-        default:
-            return szr ? launch_ring<BITS, 32, 2, 4, true>(a, p.split, s)
-                       : launch_ring<BITS, 32, 2, 4, false>(a, p.split, s);
+        default: break;
     }
+    const int sz = ring_sz_mode(a, a.w->K / kBK / p.split);
+    if (p.cfg == 3) {
+        return sz == kSzRow    ? launch_ring<BITS, 128, 2, 4, kSzRow>(a, p.split, s)
+               : sz == kSzRegs ? launch_ring<BITS, 128, 2, 4, kSzRegs>(a, p.split, s)
+                               : launch_ring<BITS, 128, 2, 4, kSzDma>(a, p.split, s);
+    }
+    return sz == kSzRow    ? launch_ring<BITS, 32, 2, 4, kSzRow>(a, p.split, s)
+           : sz == kSzRegs ? launch_ring<BITS, 32, 2, 4, kSzRegs>(a, p.split, s)
+                           : launch_ring<BITS, 32, 2, 4, kSzDma>(a, p.split, s);
 }
 
 }  // namespace

@@ -32,6 +32,14 @@
 // descriptor here has no row stride, so the compact form is the one the INT2
 // GEMM can read.  Scales and zeros are overwritten element for element by
 // the lane that read them.
+//
+// Per-row groups (group size K; the same section's Phase 2b meets them) take
+// k_requant_4to2_row: one workgroup per row holds the row's INT4 words in
+// registers, reduces the row's smallest and largest code through LDS, builds
+// the same 16-entry table from the row's scale and zero (threads 0..15, one
+// entry each), and after that barrier writes the INT2 row: every read of the
+// row precedes every write, so in place row n may overwrite INT4 row n / 2,
+// and rows run in the same launch order [0, 1), [1, 2), [2, 4), ...
 #include "device.h"
 #include "internal.h"
 
@@ -115,6 +123,92 @@ __global__ __launch_bounds__(256) void k_requant_4to2(
     if (bad) atomicOr(status, 1);
 }
 
+// Per-row groups: workgroup x covers row row0 + x; thread t takes
+// INT2 words t, t + 256, ... of the row (INT4 words 2j, 2j + 1 for INT2 word j).
+constexpr int kRowPairs = kRequantRowMaxK / 16 / 256;  // INT2 words per thread, at most
+
+__global__ __launch_bounds__(256) void k_requant_4to2_row(
+    const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
+    uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status) {
+    __shared__ int red[2][4];
+    __shared__ uint32_t tab[16];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t n = row0 + blockIdx.x;
+    const int words2 = K / 16;
+    const double s4 = f16_bits_to_f64(scales4[n]), z4 = f16_bits_to_f64(zeros4[n]);
+    u32x2 w[kRowPairs];
+    int qmin = 15, qmax = 0;
+#pragma unroll
+    for (int i = 0; i < kRowPairs; ++i) {
+        const int j = t + 256 * i;
+        w[i] = j < words2 ? *(const u32x2*)(codes4 + n * (K / 8) + 2 * j) : u32x2{0u, 0u};
+        if (j < words2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int q = (int)((w[i][h] >> (16 * (c & 1) + 4 * (c >> 1))) & 0xFu);
+                    qmin = q < qmin ? q : qmin;
+                    qmax = q > qmax ? q : qmax;
+                }
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const int a = __shfl_xor(qmin, m), b = __shfl_xor(qmax, m);
+        qmin = a < qmin ? a : qmin;
+        qmax = b > qmax ? b : qmax;
+    }
+    if (lane == 0) {
+        red[0][wave] = qmin;
+        red[1][wave] = qmax;
+    }
+    __syncthreads();
+    qmin = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+    qmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    const double wa = ((double)qmin - z4) * s4, wb = ((double)qmax - z4) * s4;
+    const double lo = fmin(0.0, fmin(wa, wb)), hi = fmax(0.0, fmax(wa, wb));
+    uint16_t s_store = f64_to_f16_bits((hi - lo) / 3.0);
+    double s2 = f16_bits_to_f64(s_store);
+    const bool bad = !isfinite(s4) || !isfinite(z4) || !isfinite(s2);
+    if (s2 == 0.0) {
+        s2 = 1.0;
+        s_store = 0x3c00;  // 1.0
+    }
+    double z2 = rint(-lo / s2);
+    z2 = z2 < 0.0 ? 0.0 : (z2 > 3.0 ? 3.0 : z2);
+    if (t < 16) {
+        double q = rint((((double)t - z4) * s4) / s2) + z2;
+        q = q >= 0.0 ? q : 0.0;  // also maps NaN to 0 (reported via status)
+        q = q > 3.0 ? 3.0 : q;
+        tab[t] = (uint32_t)q;
+    }
+    __syncthreads();
+    uint32_t table = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) table |= tab[v] << (2 * v);
+#pragma unroll
+    for (int i = 0; i < kRowPairs; ++i) {
+        const int j = t + 256 * i;
+        if (j >= words2) continue;
+        uint32_t out = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t q4 = (w[i][h] >> (16 * (c & 1) + 4 * (c >> 1))) & 0xFu;
+                const int jj = 8 * h + c;  // code index inside the INT2 word
+                out |= ((table >> (2 * q4)) & 3u) << (16 * (jj & 1) + 2 * (jj >> 1));
+            }
+        codes2[n * words2 + j] = out;
+    }
+    if (t == 0) {
+        scales2[n] = s_store;
+        zeros2[n] = f64_to_f16_bits(z2);
+        if (bad) atomicOr(status, 1);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
@@ -132,6 +226,18 @@ hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in
                                                 gcount, c2, s2, z2, status);
         return hipGetLastError();
     };
+    if (per_row(w4)) {
+        auto rows = [&](int64_t row0, int64_t count) {
+            k_requant_4to2_row<<<(unsigned)count, 256, 0, s>>>(w4.codes, w4.scales, w4.zeros, K,
+                                                               (int)row0, c2, s2, z2, status);
+            return hipGetLastError();
+        };
+        if (!in_place) return rows(0, N);
+        hipError_t e = rows(0, 1);
+        for (int64_t lo = 1; e == hipSuccess && lo < N; lo *= 2)
+            e = rows(lo, (2 * lo < N ? 2 * lo : N) - lo);
+        return e;
+    }
     if (!in_place) return run(0, N, 0, groups);
     hipError_t e = run(0, 1, 0, 1);
     for (int lo = 1; e == hipSuccess && lo < groups; lo *= 2)

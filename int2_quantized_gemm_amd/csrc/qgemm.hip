@@ -52,11 +52,11 @@ int check_weight(const qg_weight* w, const char* fn, const char* name) {
     if (w->bits != 4 && w->bits != 2)
         return fail(QG_EUNSUPPORTED, "%s: %s.bits = %d, layout v1 supports 4 and 2", fn, name,
                     w->bits);
-    if (w->group != 128)
-        return fail(QG_EUNSUPPORTED, "%s: %s.group = %d, layout v1 requires 128", fn, name,
-                    w->group);
     if (w->K <= 0 || w->K % 128 != 0)
         return fail(QG_EINVAL, "%s: %s.K = %d must be a positive multiple of 128", fn, name, w->K);
+    if (w->group != 128 && w->group != w->K)
+        return fail(QG_EUNSUPPORTED, "%s: %s.group = %d, layout v1 has groups of 128 or per-row "
+                                     "groups (group = K = %d)", fn, name, w->group, w->K);
     if (w->N <= 0) return fail(QG_EINVAL, "%s: %s.N = %d must be positive", fn, name, w->N);
     if (!w->codes || !w->scales || !w->zeros)
         return fail(QG_EINVAL, "%s: %s has a NULL codes/scales/zeros pointer", fn, name);
@@ -177,6 +177,7 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     const bool fuse_first = qg::gemm_fuses_layernorm(gate ? blk->gate.bits : blk->up.bits, M, D, F);
     // At M == 1 a gated block runs gate and up as one SwiGLU pair launch.
     const bool pair = gate && fuse_swiglu && blk->gate.bits == blk->up.bits &&
+                      blk->gate.group == blk->up.group &&
                       qg::gemm_fuses_swiglu(blk->up.bits, M, D, F);
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
         qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
@@ -321,8 +322,9 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     const char* fn = "qg_pack";
     if (bits != 4 && bits != 2)
         return fail(QG_EUNSUPPORTED, "%s: bits = %d, layout v1 supports 4 and 2", fn, bits);
-    if (group != 128)
-        return fail(QG_EUNSUPPORTED, "%s: group = %d, layout v1 requires 128", fn, group);
+    if (group != 128 && group != K)
+        return fail(QG_EUNSUPPORTED, "%s: group = %d, layout v1 has groups of 128 or per-row "
+                                     "groups (group = K = %d)", fn, group, K);
     if (K <= 0 || K % 128 != 0)
         return fail(QG_EINVAL, "%s: K = %d must be a positive multiple of 128", fn, K);
     if (N <= 0) return fail(QG_EINVAL, "%s: N = %d must be positive", fn, N);
@@ -347,7 +349,7 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     }
     int* st = g_pack_status[dev];
     if ((e = hipMemsetAsync(st, 0, sizeof(int), s)) != hipSuccess) return hip_fail(fn, e);
-    if ((e = qg::launch_pack(W, ldw, K, N, bits, codes, scales, zeros, st, s)) != hipSuccess)
+    if ((e = qg::launch_pack(W, ldw, K, N, bits, group, codes, scales, zeros, st, s)) != hipSuccess)
         return hip_fail(fn, e);
     int host = 0;
     if ((e = hipMemcpyAsync(&host, st, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -378,7 +380,13 @@ int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
     if (w2->K != w4->K || w2->N != w4->N)
         return fail(QG_EINVAL, "%s: w2 is %d x %d but w4 is %d x %d (K x N)", fn, w2->K, w2->N,
                     w4->K, w4->N);
-    const int groups = w4->K / 128;
+    if (w2->group != w4->group)
+        return fail(QG_EINVAL, "%s: w2.group = %d must equal w4.group = %d", fn, w2->group,
+                    w4->group);
+    if (w4->group != 128 && w4->K > qg::kRequantRowMaxK)
+        return fail(QG_EUNSUPPORTED, "%s: per-row groups need K <= %d (K = %d)", fn,
+                    qg::kRequantRowMaxK, w4->K);
+    const int groups = w4->K / w4->group;
     const size_t c4 = (size_t)w4->N * (w4->K / 8) * 4, c2 = (size_t)w4->N * (w4->K / 16) * 4;
     const size_t sz = (size_t)w4->N * groups * 2;
     const void* in[3] = {w4->codes, w4->scales, w4->zeros};

@@ -46,6 +46,7 @@ def _gemm(fn, w, X=FAKE, ldx=2048, Y=FAKE, ldy=2048, M=1, ws=None, ws_bytes=0):
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(bits=3), qg.QG_EUNSUPPORTED, "bits"),
     (dict(group=64), qg.QG_EUNSUPPORTED, "group"),
+    (dict(group=1024), qg.QG_EUNSUPPORTED, "group"),       # neither 128 nor K
     (dict(K=100), qg.QG_EINVAL, "K"),
     (dict(K=0), qg.QG_EINVAL, "K"),
     (dict(N=0), qg.QG_EINVAL, "N"),
@@ -66,6 +67,13 @@ def test_gemm_rejects_bad_weight(kw, code, needle):
 def test_gemm_rejects_bad_operands(kw, needle):
     assert _gemm(qg.lib.qg_gemm_int4, _w(), **kw) == qg.QG_EINVAL
     assert needle in qg.qg_last_error()
+
+
+def test_gemm_accepts_per_row_groups():
+    """group == K passes the weight check: the call then stops at the next
+    operand check (ldy too small), before any launch."""
+    assert _gemm(qg.lib.qg_gemm_int4, _w(group=2048), ldy=100) == qg.QG_EINVAL
+    assert "ldy" in qg.qg_last_error()
 
 
 def test_gemm_bits_must_match_entry_point():
@@ -175,9 +183,20 @@ _C2, _S2, _Z2 = FAKE + (8 << 20), FAKE + (12 << 20), FAKE + (13 << 20)
     (dict(), dict(scales=_C4), "overlaps input codes"),
     (dict(), dict(zeros=_S4 + 2), "overlaps input scales"),
     (dict(), dict(codes=_S2), "outputs overlap"),
+    (dict(group=2048), dict(), "group"),                        # per-row in, groups of 128 out
+    (dict(), dict(group=2048), "group"),
 ])
 def test_requant_rejects_bad_arguments(w4kw, w2kw, needle):
     w4 = _w(**{**dict(bits=4, codes=_C4, scales=_S4, zeros=_Z4), **w4kw})
     w2 = _w(**{**dict(bits=2, codes=_C2, scales=_S2, zeros=_Z2), **w2kw})
     assert _rq(w4, w2) == qg.QG_EINVAL
     assert needle in qg.qg_last_error()
+
+
+def test_requant_per_row_k_limit():
+    """Per-row re-quantisation holds a row in one workgroup: K <= 32768."""
+    K = 65536
+    w4 = _w(bits=4, K=K, N=4, group=K, codes=_C4, scales=_S4, zeros=_Z4)
+    w2 = _w(bits=2, K=K, N=4, group=K, codes=_C2, scales=_S2, zeros=_Z2)
+    assert _rq(w4, w2) == qg.QG_EUNSUPPORTED
+    assert "per-row" in qg.qg_last_error()
