@@ -16,12 +16,14 @@
 namespace qg {
 namespace {
 
-template <int BITS>
+// PER_ROW: gl = K (runtime); otherwise gl = 128, a compile-time loop bound.
+template <int BITS, bool PER_ROW>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64_t ldw, int K,
-                                              int N, int gl, uint32_t* __restrict__ codes,
+                                              int N, uint32_t* __restrict__ codes,
                                               uint16_t* __restrict__ scales,
                                               uint16_t* __restrict__ zeros, int* status) {
     using F = Fmt<BITS>;
+    const int gl = PER_ROW ? K : kGroup;
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     const int g = blockIdx.y;
     if (n >= N) return;
@@ -121,10 +123,15 @@ hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int 
                        uint32_t* codes, qg_half* scales, qg_half* zeros, int* status,
                        hipStream_t s) {
     dim3 grid((N + 255) / 256, K / group);
-    if (bits == 4)
-        k_pack<4><<<grid, 256, 0, s>>>(W, ldw, K, N, group, codes, scales, zeros, status);
+    const bool row = group != kGroup;
+    if (bits == 4 && row)
+        k_pack<4, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+    else if (bits == 4)
+        k_pack<4, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+    else if (row)
+        k_pack<2, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
     else
-        k_pack<2><<<grid, 256, 0, s>>>(W, ldw, K, N, group, codes, scales, zeros, status);
+        k_pack<2, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
     return hipGetLastError();
 }
 
