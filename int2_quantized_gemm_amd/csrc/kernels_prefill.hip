@@ -640,14 +640,14 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 struct Plan {
     int cfg;    // 0: 128x128 single stage, 1: 128x128 eight waves, 2: 64x64, 3: ring 128x128,
-                // 4: ring 32x128
+                // 4: ring 32x128, 5: ring 64x128
     int split;  // K parts
 };
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Up to this M the ring kernel runs 32-row tiles.
-constexpr int kMidMaxM = 256;
+// Up to this M the ring kernel always runs 32-row tiles.
+constexpr int kSmallM = 128;
 
 // Ring kernel with 32-row tiles: K split into the most parts (at most 8) that
 // keep at most 256 workgroups and at least 8 groups per part; {-1, 0} where
@@ -662,43 +662,53 @@ Plan plan_ring32(int M, int N, int groups) {
     return {-1, 0};
 }
 
+// Ring kernel with 64-row tiles: no split from 144 tiles on; below that, for
+// K of at least 32 groups, K split (parts of >= 8 groups) towards 192
+// workgroups; {-1, 0} otherwise.
+Plan plan_ring64(int M, int N, int groups) {
+    const int t64 = ceil_div(M, 64) * ceil_div(N, 128);
+    const bool whole = groups % 8 == 0 || groups <= 8;
+    if (t64 >= 144) return whole ? Plan{5, 1} : Plan{-1, 0};
+    if (groups < 32 || groups % 8 != 0) return {-1, 0};
+    int sp = 1;
+    while (sp < 8 && t64 * sp < 192 && groups % (2 * sp) == 0 && groups / (2 * sp) >= 8) sp *= 2;
+    return (groups / sp) % 8 == 0 ? Plan{5, sp} : Plan{-1, 0};
+}
 
-// Tile choice, from sweeps on MI355X over the block's four shapes, INT4 and
-// INT2, M = 17..2048.  The ring kernels (operands prefetched by LDS DMA) need
-// aligned operands (ring = false otherwise):
-//   * M <= kMidMaxM (batched decode): 32-row ring tiles (plan_ring32).  More,
-//     smaller tiles beat fewer 128-row ones here although each 32-row tile
+
+// Tile choice, from graph-timed sweeps on MI355X over the block's four
+// shapes, INT4 and INT2, M = 17..2048.  The ring kernels (operands prefetched
+// by LDS DMA) need aligned operands (ring = false otherwise):
+//   * M <= kSmallM (batched decode): 32-row ring tiles (plan_ring32).  More,
+//     smaller tiles beat fewer larger ones although each 32-row tile
 //     dequantises its B tile again: these launches are bound by per-step
-//     latency and by how many CUs have work, not by the dequantisation
-//     (0-30 % faster than the best other tile at M = 17..256);
-//   * 128-row ring tiles from 192 tiles up to 2048 (measured to 1024), and
-//     with K split into parts of at least 8 groups where K >= 4096 leaves too
-//     few tiles;
-//   * other shapes with fewer than 192 128-row tiles: 32-row ring tiles again
-//     (up to 30 % faster than the staged kernels at M = 384..1024).
-// Otherwise the staged kernels: past 2048 tiles single-stage 128x128
-// workgroups (two resident per CU overlap each other's barriers); with about
-// one tile per CU, 128x128 on eight waves splitting each step's k-slices in
-// two; with fewer tiles, 64x64 workgroups of four 32x32 waves, several
-// resident per CU, K split over up to 8 parts of at least 4 groups.
+//     latency and by how many CUs have work, not by the dequantisation;
+//   * K of >= 64 groups with >= 256 128-row tiles: 128-row ring tiles (the
+//     long prefill projection, where the 128-row tile's A reuse pays);
+//   * otherwise 64-row ring tiles (plan_ring64): two workgroups fit per CU,
+//     so one wave's dequantisation overlaps another's MFMAs on the same SIMD
+//     (5-17 % faster than 128-row tiles at M = 192..2048; a 2 x 2 wave grid
+//     that halves the A reads but doubles the dequantisation was slower);
+//   * where they would have too few tiles, 32-row ring tiles again.
+// The staged kernels remain for operands the ring cannot take: past 512
+// 128-row tiles single-stage 128x128 workgroups (two resident per CU overlap
+// each other's barriers); with about one tile per CU, 128x128 on eight waves
+// splitting each step's k-slices in two; with fewer tiles, 64x64 workgroups of
+// four 32x32 waves, several resident per CU, K split over up to 8 parts of at
+// least 4 groups.
 Plan plan_for(int M, int N, int K, bool ring) {
     const int groups = K / kBK;
     const int t128 = ceil_div(M, 128) * ceil_div(N, 128);
     const int t64 = ceil_div(M, 64) * ceil_div(N, 64);
-    if (ring && M <= kMidMaxM) {
-        const Plan p = plan_ring32(M, N, groups);
-        if (p.cfg >= 0) return p;
-    }
-    if (ring && groups % 8 == 0) {
-        if (t128 >= 192 && t128 < 2048) return {3, 1};
-        if (t128 < 192 && groups >= 32) {
-            int sp = 1;
-            while (sp < 8 && t128 * sp < 192) sp *= 2;
-            if (t128 * sp >= 192 && (groups / sp) % 8 == 0) return {3, sp};
+    if (ring) {
+        if (M <= kSmallM) {
+            const Plan p = plan_ring32(M, N, groups);
+            if (p.cfg >= 0) return p;
         }
-    }
-    if (ring && t128 < 192) {
-        const Plan p = plan_ring32(M, N, groups);
+        if (groups % 8 == 0 && groups >= 64 && t128 >= 256) return {3, 1};
+        Plan p = plan_ring64(M, N, groups);
+        if (p.cfg >= 0) return p;
+        p = plan_ring32(M, N, groups);
         if (p.cfg >= 0) return p;
     }
     if (t128 >= 512) return {0, 1};
@@ -763,6 +773,11 @@ hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
         return sz == kSzRow    ? launch_ring<BITS, 128, 2, 4, kSzRow>(a, p.split, s)
                : sz == kSzRegs ? launch_ring<BITS, 128, 2, 4, kSzRegs>(a, p.split, s)
                                : launch_ring<BITS, 128, 2, 4, kSzDma>(a, p.split, s);
+    }
+    if (p.cfg == 5) {
+        return sz == kSzRow    ? launch_ring<BITS, 64, 2, 4, kSzRow>(a, p.split, s)
+               : sz == kSzRegs ? launch_ring<BITS, 64, 2, 4, kSzRegs>(a, p.split, s)
+                               : launch_ring<BITS, 64, 2, 4, kSzDma>(a, p.split, s);
     }
     return sz == kSzRow    ? launch_ring<BITS, 32, 2, 4, kSzRow>(a, p.split, s)
            : sz == kSzRegs ? launch_ring<BITS, 32, 2, 4, kSzRegs>(a, p.split, s)

@@ -86,11 +86,14 @@ def test_gemm_long_prefill_down_proj_sampled_rows(orc):
     assert np.all(np.isfinite(Y))
 
 
-# Shapes whose tile plan runs the LDS-DMA ring kernel with 128-row tiles:
-# >= 192 output tiles of 128 x 128 (ragged M and N edges), and K = 8192 with
-# too few tiles, split into 8 parts of 8 groups.  Rows are independent, so the
-# oracle checks rows at both edges of every 128-row block.
-RING_CASES = [(300, 2048, 8200), (520, 8192, 1000), (1024, 2048, 6144)]
+# Shapes whose tile plan runs the LDS-DMA ring kernel with 64- and 128-row
+# tiles (ragged M and N edges): 64-row tiles without and with a K split (K =
+# 8192 in 4 parts of 16 groups) and with scales and zeros in registers (K of
+# 5 groups); 128-row tiles (K = 8192 with >= 256 tiles); and K of 10 groups,
+# which no ring tile takes, on the staged kernel.  Rows are independent, so
+# the oracle checks rows at both edges of every 64-row block.
+RING_CASES = [(300, 2048, 8200), (520, 8192, 1000), (1024, 2048, 6144), (1100, 8192, 4000),
+              (300, 640, 8200), (300, 1280, 8200)]
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -114,15 +117,15 @@ def test_gemm_ring_path_sampled_rows(orc, bits, M, K, N):
     torch.cuda.synchronize()
     g.check()
     Y = g.view.float().cpu().numpy()
-    rows = sorted({r for b in range(0, M, 128) for r in (b, min(b + 127, M - 1))} | {M - 1})
+    rows = sorted({r for b in range(0, M, 64) for r in (b, min(b + 63, M - 1))} | {M - 1})
     assert_close(Y[rows], orc.gemm(X.numpy()[rows], op), f"ring bits={bits} M={M} K={K} N={N}")
 
 
-# Shapes whose tile plan runs the ring kernel with 32-row tiles: M <= 256
-# (batched decode) and larger M with few 128-row tiles.  Scales and zeros come
-# by DMA for parts of whole runs of 8 groups, from registers for K of 3, 5 and
-# 7 groups; K split into 2 and 8 parts.  The last case is 1024 128-row tiles,
-# the 128-row ring's largest measured size.
+# Shapes whose tile plan runs the ring kernel with 32-row tiles: M <= 128
+# (batched decode) and larger M with too few 64-row tiles.  Scales and zeros
+# come by DMA for parts of whole runs of 8 groups, from registers for K of 3,
+# 5 and 7 groups; K split into 2 and 8 parts.  (200, 8192, 1500) and
+# (2048, 2048, 8192) take 64-row tiles (K split in 4; 2048 tiles).
 RING32_CASES = [(40, 1024, 1000), (17, 640, 300), (100, 384, 520), (33, 2048, 6144),
                 (64, 8192, 2048), (200, 8192, 1500), (384, 2048, 2048), (700, 896, 700),
                 (2048, 2048, 8192)]

@@ -48,12 +48,13 @@ def test_perrow_unpack_and_dequant_bit_exact(orc, bits):
     assert np.array_equal(f16_bits(qg.qg_dequant(p, fp16=True)), orc.half_bits(ref))
 
 
-# (M, K, N): GEMV; skinny in one part and in K parts; ring 32-row
-# tiles (one part, and K = 8192 split in 8); ring 128-row tiles (>= 192 tiles
-# of 128 x 128); the staged 64 x 64 kernel (>= 192 tiles of 128 x 128 but 7
-# groups along K, which the tile plan keeps off the ring).
+# (M, K, N): GEMV; skinny in one part and in K parts; ring 32-row tiles (one
+# part, and K = 8192 split in 8); ring 64-row tiles (K of 16 and 7 groups);
+# ring 128-row tiles (K = 8192, >= 256 tiles); the staged kernel (K of 10
+# groups, which the tile plan keeps off the ring).
 PERROW_GEMM = [(1, 2048, 1000), (1, 512, 300), (5, 2048, 200), (16, 8192, 520),
-               (40, 1024, 1000), (64, 8192, 2048), (300, 2048, 8200), (300, 896, 8200)]
+               (40, 1024, 1000), (64, 8192, 2048), (300, 2048, 8200), (300, 896, 8200),
+               (1100, 8192, 4000), (300, 1280, 8200)]
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -67,8 +68,9 @@ def test_perrow_gemm_paths(orc, bits, M, K, N):
     torch.cuda.synchronize()
     g.check()
     Y = g.view.float().cpu().numpy()
+    blk = 32 if M <= 400 else 64
     rows = list(range(M)) if M <= 64 else sorted(
-        {r for b in range(0, M, 32) for r in (b, min(b + 31, M - 1))} | {M - 1})
+        {r for b in range(0, M, blk) for r in (b, min(b + blk - 1, M - 1))} | {M - 1})
     assert_close(Y[rows], orc.gemm(X.numpy()[rows], op),
                  f"per-row bits={bits} M={M} K={K} N={N}")
 
