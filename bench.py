@@ -303,6 +303,29 @@ def extra_legs(qg, torch, workloads, args):
     del Xd, Y, p
     sync()
 
+    # Measured memory bandwidth, context for the spec peak (not a roofline
+    # peak): a device-to-device copy of 1 GiB (single pass through HBM) and of
+    # 48 MiB (source and destination MALL-resident after the first pass),
+    # bytes read + written per second; eager launches, HIP events.
+    def copy_bw(nbytes, reps):
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        sync()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        b.record()
+        sync()
+        per = a.elapsed_time(b) * 1e-3 / reps
+        del src, dst
+        return round(2 * nbytes / per / 1e9, 1)
+    out["measured_copy_bw_GB/s"] = {"hbm_1GiB": copy_bw(1 << 30, 20),
+                                    "mall_48MiB": copy_bw(48 << 20, 400),
+                                    "kind": "torch device copy, read + write, context only"}
+    sync()
+
     # INT4 -> INT2 tier switch of the measured block: the four projections
     # re-quantised out of place into preallocated INT2 weights.  Each call
     # synchronises (it reports errors), so this is the caller-visible time;
@@ -418,6 +441,10 @@ def main():
         log(f"cpu_baseline: {result['cpu_baseline']}")
     if not args.no_extra:
         result["extra"] = extra_legs(qg, torch, workloads, args)
+        # reuse gain of the loop: time of one cold (single-pass) iteration over
+        # one warm iteration of the main leg
+        cold = result["extra"]["c2_int4_block_m1_cold_l1"]["ms_per_iteration"]
+        result["extra"]["c2_reuse_gain"] = round(cold / (el / args.steps / L_MAIN * 1e3), 3)
         log(f"extra: {json.dumps(result['extra'])}")
     print(json.dumps(result), flush=True)
 
