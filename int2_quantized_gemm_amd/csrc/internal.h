@@ -73,8 +73,10 @@ enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };
 GemmPath gemm_path(int bits, int M, int K, int N);
 size_t gemm_ws_bytes(int bits, int M, int K, int N);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
-// M > 16: LDS-staged, double-buffered MFMA GEMM (kernels_prefill.hip); when it
-// splits K, a.ws must hold prefill_ws_bytes(M, N, K) bytes of FP32 partials.
+// M > 16 (and M <= 16 with K > 8192): the tiled MFMA GEMMs of
+// kernels_prefill.hip (ring kernel with 32-, 64- or 128-row tiles, or the
+// staged kernel), picked by the tile plan; when the plan splits K, a.ws must
+// hold prefill_ws_bytes(M, N, K) bytes of FP32 partials.
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t s);
 // Deterministic sum of K-split partials part[0..S)[M][N] (FP32, in split
 // order) into a.Y with a's epilogue.

@@ -518,8 +518,6 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
     return a.ln_h ? launch_gemv_ln<BITS, true>(a, s) : launch_gemv_ln<BITS, false>(a, s);
 }
 
-// K split so that each wave owns at most 4 groups: 4 waves up to K = 2048,
-// 8 up to 4096, 16 up to 8192.
 // K parts of the skinny kernel: enough that each spans at most kSkinnyMaxK.
 int skinny_parts(int K) { return (K + kSkinnyMaxK - 1) / kSkinnyMaxK; }
 

@@ -1,9 +1,18 @@
-// kernels_prefill.hip -- prefill GEMM (M > 16): Y[M][N] = X[M][K] . dequant(W)[K][N]
-// on FP16 MFMA, for the chunked-prefill row counts of the "Model" page
-// (prefill_chunk = 512 rows) and single-shot prefill.
+// kernels_prefill.hip -- tiled GEMM (M > 16): Y[M][N] = X[M][K] . dequant(W)[K][N]
+// on FP16 MFMA, for batched decode, the chunked-prefill row counts of the
+// "Model" page (prefill_chunk = 512 rows) and single-shot prefill.
 //
-// One K step is one quantisation group (128 values along K).  Per step the
-// workgroup
+// Two kernels, picked per shape by plan_for (measured tile plan, below):
+//   * k_gemm_ring (the usual one): every operand streamed into LDS by LDS DMA
+//     through rings of stages, 32-, 64- or 128-row tiles of 128 columns,
+//     described with the kernel;
+//   * k_gemm_prefill (staged): for operands the ring's DMA cannot take and
+//     shapes it does not suit, described next.
+// Both can split K into parts whose FP32 partial tiles k_splitk_reduce sums
+// in part order.
+//
+// Staged kernel: one K step is one quantisation group (128 values along K).
+// Per step the workgroup
 //   * stages the A tile (BM x 128 FP16 activations) in LDS, and
 //   * dequantises the B tile once -- BN output channels x 128 codes, each
 //     converted to fp16_rne((q - z) * s) with the exponent-bias trick -- into
