@@ -65,8 +65,8 @@ typedef uint16_t qg_half; /* IEEE binary16 bit pattern */
 
 /* One packed weight (the pages' QuantWeight: packed data, FP16 scales and
  * zeros, bits; CTX-TIER Phase 2).  bits in {4, 2}; group == 128 or group == K
- * (per-row: scales and zeros are [N][1]); K % 128 == 0; N >= 1; codes 16-byte
- * aligned; scales/zeros 2-byte aligned. */
+ * (per-row: scales and zeros are [N][1]); K % 128 == 0 and K <= 2^22; N >= 1;
+ * codes 16-byte aligned; scales/zeros 2-byte aligned. */
 typedef struct qg_weight {
     int32_t bits;
     int32_t K;
@@ -130,7 +130,7 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
 int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream);
 
 /* Y[M][N] = X[M][K] . dequant(w)[K][N] (quant_gemm, "β-Informed Deployment
- * Features" page).  X FP16 [M][ldx], Y FP16 [M][ldy], ldx >= K, ldy >= N, both
+ * Features" page).  X FP16 [M][ldx], Y FP16 [M][ldy], K <= ldx <= 2^22, ldy >= N, both
  * multiples of 8 and 16-byte aligned pointers; FP32 accumulation, one
  * round-to-nearest-even to FP16 at the end.  M == 0 is a no-op.
  * w->bits must be 4 (qg_gemm_int4) or 2 (qg_gemm_int2), like the pages'

@@ -46,14 +46,20 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Largest K and activation leading dimension (elements): the tiled kernels
+// address a tile's operands through buffer descriptors of at most 2 GiB
+// from the tile's first row (128 rows of up to 2^22 FP16 values = 1 GiB).
+constexpr int64_t kMaxK = int64_t(1) << 22;
+
 // Layout-v1 checks shared by every entry point taking a weight.
 int check_weight(const qg_weight* w, const char* fn, const char* name) {
     if (!w) return fail(QG_EINVAL, "%s: %s is NULL", fn, name);
     if (w->bits != 4 && w->bits != 2)
         return fail(QG_EUNSUPPORTED, "%s: %s.bits = %d, layout v1 supports 4 and 2", fn, name,
                     w->bits);
-    if (w->K <= 0 || w->K % 128 != 0)
-        return fail(QG_EINVAL, "%s: %s.K = %d must be a positive multiple of 128", fn, name, w->K);
+    if (w->K <= 0 || w->K % 128 != 0 || w->K > kMaxK)
+        return fail(QG_EINVAL, "%s: %s.K = %d must be a positive multiple of 128, at most %lld",
+                    fn, name, w->K, (long long)kMaxK);
     if (w->group != 128 && w->group != w->K)
         return fail(QG_EUNSUPPORTED, "%s: %s.group = %d, layout v1 has groups of 128 or per-row "
                                      "groups (group = K = %d)", fn, name, w->group, w->K);
@@ -77,9 +83,9 @@ int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half*
     if (M < 0) return fail(QG_EINVAL, "%s: M = %d must be >= 0", fn, M);
     if (M == 0) return QG_OK;
     if (!X || !Y) return fail(QG_EINVAL, "%s: X or Y is NULL", fn);
-    if (ldx < w->K || ldx % 8 != 0)
-        return fail(QG_EINVAL, "%s: ldx = %lld must be >= K = %d and a multiple of 8", fn,
-                    (long long)ldx, w->K);
+    if (ldx < w->K || ldx % 8 != 0 || ldx > kMaxK)
+        return fail(QG_EINVAL, "%s: ldx = %lld must be >= K = %d, a multiple of 8 and at most %lld",
+                    fn, (long long)ldx, w->K, (long long)kMaxK);
     if (ldy < w->N || ldy % 8 != 0)
         return fail(QG_EINVAL, "%s: ldy = %lld must be >= N = %d and a multiple of 8", fn,
                     (long long)ldy, w->N);
@@ -325,8 +331,9 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     if (group != 128 && group != K)
         return fail(QG_EUNSUPPORTED, "%s: group = %d, layout v1 has groups of 128 or per-row "
                                      "groups (group = K = %d)", fn, group, K);
-    if (K <= 0 || K % 128 != 0)
-        return fail(QG_EINVAL, "%s: K = %d must be a positive multiple of 128", fn, K);
+    if (K <= 0 || K % 128 != 0 || K > kMaxK)
+        return fail(QG_EINVAL, "%s: K = %d must be a positive multiple of 128, at most %lld", fn,
+                    K, (long long)kMaxK);
     if (N <= 0) return fail(QG_EINVAL, "%s: N = %d must be positive", fn, N);
     if (ldw < N) return fail(QG_EINVAL, "%s: ldw = %lld must be >= N = %d", fn, (long long)ldw, N);
     if (!W || !codes || !scales || !zeros)

@@ -48,6 +48,7 @@ def _gemm(fn, w, X=FAKE, ldx=2048, Y=FAKE, ldy=2048, M=1, ws=None, ws_bytes=0):
     (dict(group=64), qg.QG_EUNSUPPORTED, "group"),
     (dict(group=1024), qg.QG_EUNSUPPORTED, "group"),       # neither 128 nor K
     (dict(K=100), qg.QG_EINVAL, "K"),
+    (dict(K=(1 << 22) + 128), qg.QG_EINVAL, "K"),
     (dict(K=0), qg.QG_EINVAL, "K"),
     (dict(N=0), qg.QG_EINVAL, "N"),
     (dict(codes=0), qg.QG_EINVAL, "NULL"),
@@ -61,7 +62,8 @@ def test_gemm_rejects_bad_weight(kw, code, needle):
 
 
 @pytest.mark.parametrize("kw,needle", [
-    (dict(ldx=2040), "ldx"), (dict(ldx=2052), "ldx"), (dict(ldy=100), "ldy"),
+    (dict(ldx=2040), "ldx"), (dict(ldx=2052), "ldx"), (dict(ldx=(1 << 22) + 8), "ldx"),
+    (dict(ldy=100), "ldy"),
     (dict(M=-1), "M"), (dict(X=0), "NULL"), (dict(Y=FAKE + 2), "aligned"),
 ])
 def test_gemm_rejects_bad_operands(kw, needle):
