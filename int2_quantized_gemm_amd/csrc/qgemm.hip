@@ -257,8 +257,12 @@ uint64_t g_graph_clock = 0;
 hipStream_t g_capture_stream[64] = {nullptr};
 constexpr size_t kMaxGraphs = 32;
 
-hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
-                      const LoopLayout& L, bool fuse_swiglu, hipGraphExec_t* out) {
+// Launches the cached graph for these arguments on stream s, capturing and
+// instantiating it first if needed.  The launch happens under the cache lock,
+// so no other thread can evict (destroy) the graph between lookup and launch.
+hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters,
+                             void* scratch, const LoopLayout& L, bool fuse_swiglu,
+                             hipStream_t s) {
     LoopKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
     key.blk = *blk;
@@ -274,8 +278,7 @@ hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, v
     for (LoopGraph& g : g_graphs) {
         if (g.key == key) {
             g.last_use = ++g_graph_clock;
-            *out = g.exec;
-            return hipSuccess;
+            return hipGraphLaunch(g.exec, s);
         }
     }
     hipStream_t& cs = g_capture_stream[key.device];
@@ -306,8 +309,7 @@ hipError_t loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters, v
         g_graphs.erase(g_graphs.begin() + lru);
     }
     g_graphs.push_back({key, exec, ++g_graph_clock});
-    *out = exec;
-    return hipSuccess;
+    return hipGraphLaunch(exec, s);
 }
 
 // Per-device status word for qg_pack and qg_requant_4to2 (library-owned, freed by
@@ -517,9 +519,7 @@ int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t 
     if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled()) {
         e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, s);
     } else {
-        hipGraphExec_t exec = nullptr;
-        e = loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, &exec);
-        if (e == hipSuccess) e = hipGraphLaunch(exec, s);
+        e = launch_loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, s);
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
