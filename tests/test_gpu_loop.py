@@ -277,3 +277,41 @@ def test_loop_gated_mixed_bits_block(orc):
     href, last = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
     _check_h(h.cpu().numpy(), href, "mixed-bits gated h")
     _check_scratch(qg.scratch_views(blk, M, scratch), last, slice(None), "mixed-bits gated")
+
+
+def test_loop_graph_cache_from_threads(orc, monkeypatch):
+    """Four threads run the loop on 48 distinct residual/scratch pairs (48
+    cached graphs, more than the cache holds, so evictions interleave with
+    other threads' lookups and launches); every result equals the direct
+    enqueue of the same call."""
+    import threading
+    D, F, M, L = 256, 512, 1, 2
+    inp, blk, _ = _blocks(orc, M, 4, D, F, seed=77)
+    h0 = inp.X.float().cuda()
+    monkeypatch.setenv("QG_LOOP_GRAPHS", "0")
+    ref_s = qg.alloc_loop_scratch(blk, M)
+    ref = h0.clone()
+    qg.qg_loop_range(blk, ref, 0, L, ref_s)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("QG_LOOP_GRAPHS", "1")
+    hs = [h0.clone() for _ in range(48)]
+    scratches = [qg.alloc_loop_scratch(blk, M) for _ in range(48)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            for i in range(t, 48, 4):
+                qg.qg_loop_range(blk, hs[i], 0, L, scratches[i])
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, h in enumerate(hs):
+        assert torch.equal(h, ref), f"call {i}"
