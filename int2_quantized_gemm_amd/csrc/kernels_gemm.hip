@@ -4,8 +4,8 @@
 //
 // Three kernel families, chosen by M:
 //   * k_gemv (M == 1): bandwidth-bound GEMV.  Lanes split K: each lane loads
-//     16 contiguous bytes of packed codes per chunk (a wave reads a contiguous
-//     1 KiB run of a row), converts codes with the exponent-bias trick and
+//     the 32 contiguous codes of a chunk (16 bytes INT4, 8 bytes INT2; a wave
+//     reads a contiguous run of a row), converts codes with the exponent-bias trick and
 //     accumulates x . (1024 + 2^j q) with v_dot2_f32_f16; bias, zero point and
 //     the per-group scale are applied once per lane chunk.  Lane partials of a
 //     row are combined by a fixed xor-butterfly (deterministic).  Optionally
@@ -23,6 +23,8 @@
 // a 128-k group, lane quarter c = l / 16 owns k in [32c, 32c + 32) and MFMA j
 // (j = 0..3) consumes its k in [32c + 8j, 32c + 8j + 8).  The accumulator
 // holds D[4*(l/16) + r][l % 16] in register r.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -31,7 +33,11 @@ namespace {
 
 // ------------------------------------------------------------------ GEMV ----
 
-// Dot products of one lane chunk (4 packed words) with its activations.
+// Dot products of one lane chunk (32 codes: WPL = b packed words) with its
+// activations.  The chunk holds 32 codes for both widths, so an INT2 lane does
+// the same decode and activation work per chunk as an INT4 lane and moves half
+// the bytes (16-byte chunks would double the activation loads and the
+// arithmetic per byte of INT2 codes).
 // Codes 2i and 2i+1 of a word sit at bits b*i and 16 + b*i.  Rather than
 // shifting every pair down, a word and its copy shifted right by 8 are each
 // masked at the NC = 8/b code positions of a byte: mask class j keeps the
@@ -45,15 +51,17 @@ struct GemvMath {
     using F = Fmt<BITS>;
     static constexpr int NC = 8 / BITS;   // mask classes
     static constexpr int PPW = 16 / BITS;  // FP16 pairs per word (= 2 * NC)
+    static constexpr int WPL = BITS;       // words per lane chunk (32 codes)
+    static constexpr int PAIRS = 16;       // FP16 activation pairs per chunk
+    using Chunk = std::conditional_t<BITS == 4, u32x4, u32x2>;
 
     // Pair index (relative to the chunk) of class j, half h (h = 1: word >> 8).
     static __device__ __forceinline__ int pair(int q, int h, int j) { return q * PPW + j + NC * h; }
 
-    static __device__ __forceinline__ void accumulate(const u32x4& w4, const f16x2* xp,
+    static __device__ __forceinline__ void accumulate(const Chunk& w, const f16x2* xp,
                                                       float acc[NC]) {
-        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < WPL; ++q) {
             const uint32_t v[2] = {w[q], w[q] >> 8};
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -71,7 +79,7 @@ struct GemvMath {
 #pragma unroll
         for (int j = 0; j < NC; ++j) xs[j] = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < WPL; ++q)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -90,8 +98,8 @@ struct GemvMath {
     }
 };
 
-// LPR lanes cover one row per chunk of 4*LPR words; CPR chunks per row;
-// 64/LPR rows per wave step; U row steps per wave; K = 4*LPR*CPR*(32/b) is a
+// LPR lanes cover one row per chunk of 32*LPR codes; CPR chunks per row;
+// 64/LPR rows per wave step; U row steps per wave; K = 32*LPR*CPR is a
 // compile-time constant of each variant.  With LN, the activations are
 // fp16(LayerNorm(hln)): the workgroup's 256 threads normalise the row once
 // (mean, then population variance of the centred values, eps 1e-5, reduced
@@ -120,8 +128,9 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     using F = Fmt<BITS>;
     using G = GemvMath<BITS>;
     constexpr int RPW = 64 / LPR;
-    constexpr int PAIRS = 4 * F::kPairsPerWord;  // FP16 pairs of x per lane and chunk
-    constexpr int K = 4 * LPR * CPR * F::kCodesPerWord;
+    constexpr int WPL = G::WPL;
+    constexpr int PAIRS = G::PAIRS;  // FP16 pairs of x per lane and chunk
+    constexpr int K = 32 * LPR * CPR;
     constexpr int wpr = K / F::kCodesPerWord;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
 
     // Issue the weight loads of this wave first; the activations and their
     // LayerNorm are computed while they are in flight.
-    u32x4 wv[NW][U][CPR];
+    typename G::Chunk wv[NW][U][CPR];
     uint16_t sv[NW][U][CPR], zv[NW][U][CPR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -142,14 +151,15 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         for (int b = 0; b < NW; ++b)
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
-                const int wi = c * LPR * 4 + sub * 4;
+                const int wi = (c * LPR + sub) * WPL;
                 if (row < N) {
-                    wv[b][u][c] = *(const u32x4*)(W.codes[b] + (int64_t)row * wpr + wi);
+                    wv[b][u][c] =
+                        *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * wpr + wi);
                     const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
                     sv[b][u][c] = W.scales[b][sg];
                     zv[b][u][c] = W.zeros[b][sg];
                 } else {
-                    wv[b][u][c] = u32x4{0, 0, 0, 0};
+                    wv[b][u][c] = typename G::Chunk{};
                     sv[b][u][c] = 0;
                     zv[b][u][c] = 0;
                 }
@@ -206,14 +216,14 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         if (!active) return;
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
-            const int p0 = (c * LPR * 4 + sub * 4) * F::kCodesPerWord / 2;
+            const int p0 = (c * LPR + sub) * 16;
 #pragma unroll
             for (int i = 0; i < PAIRS; ++i) xr[c][i] = as_f16x2(xl[p0 + i]);
         }
     } else {
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
-            const int k0 = (c * LPR * 4 + sub * 4) * F::kCodesPerWord;
+            const int k0 = (c * LPR + sub) * 32;
             const u32x4* xp = (const u32x4*)(X + k0);
 #pragma unroll
             for (int v = 0; v < PAIRS / 4; ++v) {
@@ -422,27 +432,30 @@ struct GemvShape {
 };
 
 GemvShape gemv_shape(int bits, int K) {
-    const int quads = K * bits / 128;  // 16-byte lane chunks per row
+    (void)bits;  // a lane chunk is 32 codes for both widths
+    const int chunks = K / 32;  // lane chunks per row
     GemvShape s{0, 0, false};
-    if (quads >= 64) {
-        if (quads % 64) return s;
+    if (chunks >= 64) {
+        if (chunks % 64) return s;
         s.lpr = 64;
-        s.cpr = quads / 64;
+        s.cpr = chunks / 64;
         s.ok = s.cpr == 1 || s.cpr == 2 || s.cpr == 4 || s.cpr == 8;
     } else {
-        s.lpr = quads;
+        s.lpr = chunks;
         s.cpr = 1;
-        s.ok = quads == 16 || quads == 32;
+        s.ok = chunks == 16 || chunks == 32;
     }
     return s;
 }
 
 // Rows per wave U: several rows per wave amortise the activations held in
 // registers (and the fused LayerNorm) but cut the number of waves in flight.
-// Measured on MI355X with the loop block's weights cache-resident: U = 4 from
-// 8192 row steps (FFN up), U = 2 from 2048 (QKV, out, down), else U = 1; at
-// most 8 outstanding 16-byte code loads per lane (U * CPR * NW <= 8, NW = 2
-// for the SwiGLU pair).
+// Measured on MI355X inside the looped block with its weights cache-resident
+// (D = 2048, F = 8192, M = 1): U = 2 from 2048 row steps (QKV, out, up, down,
+// the SwiGLU pair), else U = 1.  U = 4 on the 8192-step FFN projections was
+// even for INT4 and 2-6 % slower per iteration for INT2 and the SwiGLU pair;
+// U = 1 and U = 4 on the 2048-step ones were slower.  At most 8 outstanding
+// code loads per lane (U * CPR * NW <= 8, NW = 2 for the SwiGLU pair).
 template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
 hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     static_assert(U * CPR * NW <= 8, "at most 8 code loads per lane");
@@ -460,11 +473,11 @@ hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The fused LayerNorm needs K = 4*LPR*CPR*(32/b) to be a multiple of 1024 and
+// The fused LayerNorm needs K = 32*LPR*CPR to be a multiple of 1024 and
 // at most 8192 (the LN input is a residual row of D <= 8192 values).
 template <int BITS, int LPR, int CPR>
 constexpr bool ln_variant_ok() {
-    constexpr int K = 4 * LPR * CPR * (32 / BITS);
+    constexpr int K = 32 * LPR * CPR;
     return K % 1024 == 0 && K <= 8192;
 }
 
@@ -477,9 +490,6 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
     const int steps = (a.w->N + RPW - 1) / RPW;
     if (a.w2 != nullptr) {  // SwiGLU pair: two weights per row step
         if constexpr (CPR <= 4) {
-            if constexpr (CPR == 1) {
-                if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN, 2>(a, s);
-            }
             if constexpr (CPR <= 2) {
                 if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 2>(a, s);
             }
@@ -487,9 +497,6 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
         } else {
             return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_swiglu
         }
-    }
-    if constexpr (CPR <= 2) {
-        if (steps >= 8 * 1024) return launch_gemv_u<BITS, LPR, CPR, 4, LN, 1>(a, s);
     }
     if constexpr (CPR <= 4) {
         if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 1>(a, s);
