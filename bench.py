@@ -23,7 +23,8 @@ The JSON line also carries
     sample of the same workload (whole L=8 steps for ~10 s);
   * extra: the other measured workloads (single-pass INT4 GEMM over a 535 MB
     rotation pool, cold single-pass block, M=512 prefill TFLOP/s, the INT2
-    block, M=16 decode for L=32 and the M=2048 down projection).
+    block, M=16 decode for L=32 and the M=2048 down projection), and as
+    context the vendor library's dense FP16 GEMM on the same prefill shapes.
 Diagnostics go to stderr; stdout holds the one JSON line.
 """
 from __future__ import annotations
@@ -324,6 +325,30 @@ def extra_legs(qg, torch, workloads, args):
     out["measured_copy_bw_GB/s"] = {"hbm_1GiB": copy_bw(1 << 30, 20),
                                     "mall_48MiB": copy_bw(48 << 20, 400),
                                     "kind": "torch device copy, read + write, context only"}
+    sync()
+
+    # Dense FP16 GEMM of the vendor library (torch.matmul -> hipBLASLt) on the
+    # same shapes as C3's projections at M = 512 and as C5b: what an
+    # unquantised FP16 weight reaches on this chip at these sizes, context for
+    # the MFMA fractions above (not part of the measured path).
+    def dense(M, K, N):
+        a = torch.randn(M, K, device=dev, dtype=torch.float16)
+        w = torch.randn(K, N, device=dev, dtype=torch.float16)
+        y = torch.empty(M, N, device=dev, dtype=torch.float16)
+        t = graph_leg(torch, lambda i: torch.matmul(a, w, out=y), 20, replays=5)
+        del a, w, y
+        return t
+    c3_shapes = {"qkv": (512, D, 3 * D), "out": (512, D, D), "up": (512, D, F), "down": (512, F, D)}
+    c3_t = {k: dense(*v) for k, v in c3_shapes.items()}
+    c5b_t = dense(2048, 8192, 2048)
+    c3_sum = sum(c3_t.values())
+    out["dense_fp16_library"] = {
+        "kind": "torch.matmul FP16 x FP16 (hipBLASLt), graph-timed, context only",
+        "c3_projections_us": {k: round(v * 1e6, 2) for k, v in c3_t.items()},
+        "c3_four_projections_TFLOP/s": round(block_flops(512) / c3_sum / 1e12, 1),
+        "c3_four_projections_frac_mfma": round(block_flops(512) / c3_sum / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "c5b_us": round(c5b_t * 1e6, 2),
+        "c5b_TFLOP/s": round(2.0 * 2048 * 8192 * 2048 / c5b_t / 1e12, 1)}
     sync()
 
     # INT4 -> INT2 tier switch of the measured block: the four projections
