@@ -11,9 +11,9 @@
 //     row are combined by a fixed xor-butterfly (deterministic).  Optionally
 //     the activations are the LayerNorm of the FP32 residual, computed in the
 //     prologue (the loop block's QKV and up projections).
-//   * k_gemm_skinny (2 <= M <= 16): one 16-row MFMA tile of output channels per
-//     workgroup, K split over the workgroup's waves and reduced through LDS in
-//     wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A (M padded to 16)
+//   * k_gemm_skinny (2 <= M <= 16): one or two 16-row MFMA tiles of output
+//     channels per workgroup, K split over the workgroup's waves and reduced
+//     through LDS in wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A (M padded to 16)
 //     and dequantised weights as B.
 //   * M > 16: the LDS-staged MFMA GEMM of kernels_prefill.hip.
 //
@@ -330,9 +330,9 @@ __device__ __forceinline__ void load_a(const uint16_t* xrow, bool valid, int g, 
 
 // ---------------------------------------------------------------- skinny ----
 
-// 2 <= M <= 16.  A workgroup of four waves computes 16 output channels over
-// one K part (at most kSkinnyMaxK values; K is cut into S parts, summed by
-// k_splitk_reduce when S > 1).  The activation rows of the part are staged
+// 2 <= M <= 16.  A workgroup of four waves computes NT tiles of 16 output
+// channels over one K part (at most kSkinnyMaxK values; K is cut into S
+// parts, summed by k_splitk_reduce when S > 1).  The activation rows of the part are staged
 // once in LDS -- 16 rows (rows past M are zero or unused) of R values,
 // 16-byte chunk ci of row m at chunk slot ci ^ (m % 16), so the fragment
 // reads of the 16 rows hit distinct banks -- by LDS DMA of contiguous row
@@ -342,41 +342,54 @@ __device__ __forceinline__ void load_a(const uint16_t* xrow, bool valid, int g, 
 // for M = 16, K = 8192, N = 2048).  Wave w takes the part's groups w, w+4, ...;
 // the four partial tiles are summed through LDS in wave order.  (Normalising
 // h inside this kernel, as the GEMV does, costs more than the LayerNorm
-// kernel: every workgroup must read all M rows of h.)
+// kernel: every workgroup must read all M rows of h.)  NT = 2 feeds each A
+// fragment read to two MFMAs and halves the activation staging per weight
+// byte; it is used while the launch keeps at least kSkinnyPairMinWgs
+// workgroups (measured on MI355X, M = 2..16: 9-14 % faster for the loop
+// block's QKV, FFN-up and K-split down projections, 14 % slower for the
+// 2048-channel out projection, whose 64 workgroups leave most CUs idle;
+// NT = 4 was slower everywhere).  Each output's MFMA chain is the same for
+// every NT, so the results are too.
 constexpr int kSkinnyMaxK = 2048;
+constexpr int kSkinnyPairMinWgs = 192;
 
-template <int BITS>
+template <int BITS, int NT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz, int K,
     int N, int S, OutEpi out, float* __restrict__ part) {
+    static_assert(NT == 1 || NT == 2, "one or two column tiles (wave t stores tile t)");
     constexpr int kMaxGpw = kSkinnyMaxK / kGroup / 4;  // groups per wave
     __shared__ __attribute__((aligned(1024))) uint8_t xs[16 * kSkinnyMaxK * 2];
-    __shared__ f32x4 red[4][64];
+    __shared__ f32x4 red[4][NT][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, c = lane >> 4;
-    const int n = blockIdx.x * 16 + nl;
-    const bool nvalid = n < N;
     const int groups = K / kGroup;
     const int p = blockIdx.y;
     const int gbeg = (int)((int64_t)groups * p / S);
     const int gcnt = (int)((int64_t)groups * (p + 1) / S) - gbeg;  // <= kSkinnyMaxK / 128
     const int cpr = gcnt * 16;  // 16-byte chunks per staged row
-    const int nr = nvalid ? n : N - 1;
-    const uint32_t* crow = codes + (int64_t)nr * (K / Fmt<BITS>::kCodesPerWord);
 
-    // weights of this wave's groups first (rows past N clamped, zeroed by scale)
-    LaneCodes<BITS> lc[kMaxGpw];
-    uint16_t sb[kMaxGpw], zb[kMaxGpw];
+    // weights of this wave's groups first, for each column tile (rows past N
+    // clamped, zeroed by scale)
+    LaneCodes<BITS> lc[NT][kMaxGpw];
+    uint16_t sb[NT][kMaxGpw], zb[NT][kMaxGpw];
 #pragma unroll
-    for (int i = 0; i < kMaxGpw; ++i) {
-        const int gi = wave + 4 * i;
-        if (gi < gcnt) {
-            const int g = gbeg + gi;
-            lc[i].load(crow, g, c);
-            sb[i] = nvalid ? scales[sz.at(nr, g)] : (uint16_t)0;
-            zb[i] = zeros[sz.at(nr, g)];
+    for (int t = 0; t < NT; ++t) {
+        const int n = (blockIdx.x * NT + t) * 16 + nl;
+        const bool nvalid = n < N;
+        const int nr = nvalid ? n : N - 1;
+        const uint32_t* crow = codes + (int64_t)nr * (K / Fmt<BITS>::kCodesPerWord);
+#pragma unroll
+        for (int i = 0; i < kMaxGpw; ++i) {
+            const int gi = wave + 4 * i;
+            if (gi < gcnt) {
+                const int g = gbeg + gi;
+                lc[t][i].load(crow, g, c);
+                sb[t][i] = nvalid ? scales[sz.at(nr, g)] : (uint16_t)0;
+                zb[t][i] = zeros[sz.at(nr, g)];
+            }
         }
     }
 
@@ -393,34 +406,46 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
     lds_barrier();
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc = zero4;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = zero4;
 #pragma unroll
     for (int i = 0; i < kMaxGpw; ++i) {
         const int gi = wave + 4 * i;
         if (gi < gcnt) {
-            const GroupConst gc = group_const(sb[i], zb[i]);
+            GroupConst gc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) gc[t] = group_const(sb[t][i], zb[t][i]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int ci = gi * 16 + 4 * c + j;  // row nl, k = 128 gi + 32 c + 8 j
                 const f16x8 a = *(const f16x8*)(xs + (nl * cpr + (ci ^ nl)) * 16);
-                acc = mfma16(a, lc[i].frag(j, gc), acc);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] = mfma16(a, lc[t][i].frag(j, gc[t]), acc[t]);
             }
         }
     }
-    red[wave][lane] = acc;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
-    if (wave != 0 || !nvalid) return;
-    f32x4 sum = red[0][lane];
+    // wave t sums column tile t in wave order and stores it
 #pragma unroll
-    for (int w = 1; w < 4; ++w) sum += red[w][lane];
+    for (int t = 0; t < NT; ++t) {
+        if (wave != t) continue;
+        const int n = (blockIdx.x * NT + t) * 16 + nl;
+        if (n >= N) continue;
+        f32x4 sum = red[0][t][lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int m = 4 * c + r;
-        if (m >= M) continue;
-        if (part != nullptr)
-            part[(int64_t)p * M * N + (int64_t)m * N + n] = sum[r];
-        else
-            epi_store(out, m, n, sum[r]);
+        for (int w = 1; w < 4; ++w) sum += red[w][t][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * c + r;
+            if (m >= M) continue;
+            if (part != nullptr)
+                part[(int64_t)p * M * N + (int64_t)m * N + n] = sum[r];
+            else
+                epi_store(out, m, n, sum[r]);
+        }
     }
 }
 
@@ -531,10 +556,16 @@ int skinny_parts(int K) { return (K + kSkinnyMaxK - 1) / kSkinnyMaxK; }
 template <int BITS>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     const int S = skinny_parts(a.w->K);
-    const dim3 grid((a.w->N + 15) / 16, S);
     float* part = S > 1 ? (float*)a.ws : nullptr;
-    k_gemm_skinny<BITS><<<grid, 256, 0, s>>>(a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros,
-                                             sz_idx(*a.w), a.w->K, a.w->N, S, a.out(), part);
+    const int pairs = (a.w->N + 31) / 32;
+    if ((int64_t)pairs * S >= kSkinnyPairMinWgs)
+        k_gemm_skinny<BITS, 2><<<dim3(pairs, S), 256, 0, s>>>(
+            a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N, S,
+            a.out(), part);
+    else
+        k_gemm_skinny<BITS, 1><<<dim3((a.w->N + 15) / 16, S), 256, 0, s>>>(
+            a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N, S,
+            a.out(), part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     return launch_splitk_reduce(part, S, a, s);

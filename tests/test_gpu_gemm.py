@@ -106,6 +106,21 @@ def test_gemm_skinny_k_parts(orc, bits, M, K, N):
     assert_close(Y, ref, f"skinny parts bits={bits} M={M} K={K} N={N}")
 
 
+# Shapes on which the skinny kernel takes two 16-channel tiles per workgroup
+# (launches of at least 192 workgroups): ragged N leaves the last workgroup's
+# second tile partly (N = 6168) or wholly (N = 6152, 2056, 1544) past N; with
+# and without K parts.
+SKINNY_PAIR_CASES = [(16, 2048, 6152), (3, 2048, 6168), (7, 6144, 2056), (16, 8192, 1544),
+                     (2, 2048, 8192)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", SKINNY_PAIR_CASES)
+def test_gemm_skinny_column_pairs(orc, bits, M, K, N):
+    Y, ref = _case(orc, bits, M, K, N, seed=M * 3 + K + N, ld_pad=8, ldx_pad=8)
+    assert_close(Y, ref, f"skinny pairs bits={bits} M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("M,K,N", RING_CASES)
 def test_gemm_ring_path_sampled_rows(orc, bits, M, K, N):
