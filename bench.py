@@ -103,7 +103,7 @@ def traffic_record(kernel_key: str):
 
 COPY_BYTES = 256 << 20  # calibration copy: larger than the 256 MB MALL's share it can hold
 GEMV_KEY = "gemv_int4_k8192_n2048"
-GEMV_SRC = os.path.join("int2_quantized_gemm_amd", "csrc", "kernels_gemm.hip")
+GEMV_SRC = os.path.join("int2_quantized_gemm_amd", "csrc", "kernels_gemv.hip")
 
 
 def pmc_target(qg, torch, workloads, launches: int = 50):

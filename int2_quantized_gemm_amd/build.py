@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["qgemm.hip", "kernels_pack.hip", "kernels_gemm.hip", "kernels_prefill.hip",
-           "kernels_loop.hip", "kernels_requant.hip"]
+SOURCES = ["qgemm.hip", "kernels_pack.hip", "kernels_gemm.hip", "kernels_gemv.hip",
+           "kernels_prefill.hip", "kernels_loop.hip", "kernels_requant.hip"]
 ARCH = os.environ.get("QG_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [

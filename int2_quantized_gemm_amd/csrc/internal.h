@@ -61,6 +61,16 @@ struct GemmArgs {
     OutEpi out() const { return OutEpi{Y, ldy, h, ldh, gm, ldg, (int)epi}; }
 };
 
+// ---- M == 1 GEMV (kernels_gemv.hip)
+// True when the GEMV has a lane arrangement for this K (K / 32 lane chunks of
+// 32 codes: 16 or 32 lanes per row, or 64 lanes and 1, 2, 4 or 8 chunks).
+bool gemv_supported(int bits, int K);
+// True when it also has the SwiGLU pair variant (at most 4 chunks per lane).
+bool gemv_pairs_supported(int bits, int K);
+// The GEMV of a.w (bits 4 or 2; M == 1, gemv_supported), with a.ln_h's fused
+// LayerNorm and a.w2's SwiGLU pair when set.
+hipError_t launch_gemv(const GemmArgs& a, hipStream_t s);
+
 // True when a GEMM of this shape can take its activations as the fused
 // LayerNorm of an FP32 row (the M == 1 GEMV path).
 bool gemm_fuses_layernorm(int bits, int M, int K, int N);

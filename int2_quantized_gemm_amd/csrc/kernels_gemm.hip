@@ -3,18 +3,11 @@
 // CTX-TIER section), FP16 activations, FP32 accumulation, FP16 output.
 //
 // Three kernel families, chosen by M:
-//   * k_gemv (M == 1): bandwidth-bound GEMV.  Lanes split K: each lane loads
-//     the 32 contiguous codes of a chunk (16 bytes INT4, 8 bytes INT2; a wave
-//     reads a contiguous run of a row), converts codes with the exponent-bias trick and
-//     accumulates x . (1024 + 2^j q) with v_dot2_f32_f16; bias, zero point and
-//     the per-group scale are applied once per lane chunk.  Lane partials of a
-//     row are combined by a fixed xor-butterfly (deterministic).  Optionally
-//     the activations are the LayerNorm of the FP32 residual, computed in the
-//     prologue (the loop block's QKV and up projections).
+//   * M == 1: the bandwidth-bound GEMV of kernels_gemv.hip.
 //   * k_gemm_skinny (2 <= M <= 16): one or two 16-row MFMA tiles of output
 //     channels per workgroup, K split over the workgroup's waves and reduced
-//     through LDS in wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A (M padded to 16)
-//     and dequantised weights as B.
+//     through LDS in wave order.  v_mfma_f32_16x16x32_f16 takes X rows as A
+//     (M padded to 16) and dequantised weights as B.
 //   * M > 16: the LDS-staged MFMA GEMM of kernels_prefill.hip.
 //
 // MFMA operand mapping used everywhere (16x16x32 f16): lane l supplies row
@@ -23,256 +16,11 @@
 // a 128-k group, lane quarter c = l / 16 owns k in [32c, 32c + 32) and MFMA j
 // (j = 0..3) consumes its k in [32c + 8j, 32c + 8j + 8).  The accumulator
 // holds D[4*(l/16) + r][l % 16] in register r.
-#include <type_traits>
-
 #include "device.h"
 #include "internal.h"
 
 namespace qg {
 namespace {
-
-// ------------------------------------------------------------------ GEMV ----
-
-// Dot products of one lane chunk (32 codes: WPL = b packed words) with its
-// activations.  The chunk holds 32 codes for both widths, so an INT2 lane does
-// the same decode and activation work per chunk as an INT4 lane and moves half
-// the bytes (16-byte chunks would double the activation loads and the
-// arithmetic per byte of INT2 codes).
-// Codes 2i and 2i+1 of a word sit at bits b*i and 16 + b*i.  Rather than
-// shifting every pair down, a word and its copy shifted right by 8 are each
-// masked at the NC = 8/b code positions of a byte: mask class j keeps the
-// codes at bits b*j and 16 + b*j, and OR-ing 0x6400 into both halves gives
-// the FP16 pair 1024 + 2^(b*j) * q exactly (all values stay below 2048, where
-// the FP16 spacing is 1).  Class j accumulates x . (1024 + 2^(b*j) q) in FP32
-// with v_dot2_f32_f16; the bias 1024 * sum(x) and the factor 2^(b*j) come
-// out once per chunk from precomputed activation sums.
-template <int BITS>
-struct GemvMath {
-    using F = Fmt<BITS>;
-    static constexpr int NC = 8 / BITS;   // mask classes
-    static constexpr int PPW = 16 / BITS;  // FP16 pairs per word (= 2 * NC)
-    static constexpr int WPL = BITS;       // words per lane chunk (32 codes)
-    static constexpr int PAIRS = 16;       // FP16 activation pairs per chunk
-    using Chunk = std::conditional_t<BITS == 4, u32x4, u32x2>;
-
-    // Pair index (relative to the chunk) of class j, half h (h = 1: word >> 8).
-    static __device__ __forceinline__ int pair(int q, int h, int j) { return q * PPW + j + NC * h; }
-
-    static __device__ __forceinline__ void accumulate(const Chunk& w, const f16x2* xp,
-                                                      float acc[NC]) {
-#pragma unroll
-        for (int q = 0; q < WPL; ++q) {
-            const uint32_t v[2] = {w[q], w[q] >> 8};
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int j = 0; j < NC; ++j)
-                    acc[j] = __builtin_amdgcn_fdot2(
-                        as_f16x2((v[h] & (F::kPairMask << (BITS * j))) | kBias2),
-                        xp[pair(q, h, j)], acc[j], false);
-        }
-    }
-
-    // Per-class sums of the activations of a chunk.
-    static __device__ __forceinline__ void xsums(const f16x2* xp, float xs[NC]) {
-        const f16x2 one = {(f16)1.0f, (f16)1.0f};
-#pragma unroll
-        for (int j = 0; j < NC; ++j) xs[j] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < WPL; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int j = 0; j < NC; ++j)
-                    xs[j] = __builtin_amdgcn_fdot2(xp[pair(q, h, j)], one, xs[j], false);
-    }
-
-    // sum_k x_k * (q_k - z) of the chunk, from the class accumulators.
-    static __device__ __forceinline__ float centred(const float acc[NC], const float xs[NC],
-                                                    float xs_all, float z) {
-        float t = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-            t += (acc[j] - 1024.0f * xs[j]) * (1.0f / (float)(1 << (BITS * j)));
-        return t - z * xs_all;
-    }
-};
-
-// LPR lanes cover one row per chunk of 32*LPR codes; CPR chunks per row;
-// 64/LPR rows per wave step; U row steps per wave; K = 32*LPR*CPR is a
-// compile-time constant of each variant.  With LN, the activations are
-// fp16(LayerNorm(hln)): the workgroup's 256 threads normalise the row once
-// (mean, then population variance of the centred values, eps 1e-5, reduced
-// by DPP in each wave and then in wave order through LDS), stage it in LDS
-// for the lanes to pick up, and workgroup 0 also writes it to norm_out.
-//
-// NW = 2 is the SwiGLU pair of a gated FFN: weight 0 is the gate and weight 1
-// the up projection, both of the same shape and bits.  Each row step loads
-// the same rows of both, and the lane that finishes row n stores
-// g = fp16(x . Wgate[n]) to gout[n] and fp16(silu(g) * fp16(x . Wup[n])) to
-// out.Y[n] (plain store epilogue), so one launch and one activation pass serve
-// both projections.
-struct GemvWeights {
-    const uint32_t* codes[2];
-    const uint16_t* scales[2];
-    const uint16_t* zeros[2];
-    SzIdx sz;  // scale addressing, the same for both weights
-};
-
-template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
-__global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
-                                              const float* __restrict__ hln,
-                                              uint16_t* __restrict__ norm_out,
-                                              GemvWeights W, int N, OutEpi out,
-                                              uint16_t* __restrict__ gout) {
-    using F = Fmt<BITS>;
-    using G = GemvMath<BITS>;
-    constexpr int RPW = 64 / LPR;
-    constexpr int WPL = G::WPL;
-    constexpr int PAIRS = G::PAIRS;  // FP16 pairs of x per lane and chunk
-    constexpr int K = 32 * LPR * CPR;
-    constexpr int wpr = K / F::kCodesPerWord;
-    const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const int sub = lane % LPR;
-    const int rsub = lane / LPR;
-    const int row0 = wave * U * RPW;
-    const bool active = row0 < N;
-    if (!LN && !active) return;  // (LN variants keep every wave for the barriers)
-
-    // Issue the weight loads of this wave first; the activations and their
-    // LayerNorm are computed while they are in flight.
-    typename G::Chunk wv[NW][U][CPR];
-    uint16_t sv[NW][U][CPR], zv[NW][U][CPR];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int row = row0 + u * RPW + rsub;
-#pragma unroll
-        for (int b = 0; b < NW; ++b)
-#pragma unroll
-            for (int c = 0; c < CPR; ++c) {
-                const int wi = (c * LPR + sub) * WPL;
-                if (row < N) {
-                    wv[b][u][c] =
-                        *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * wpr + wi);
-                    const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
-                    sv[b][u][c] = W.scales[b][sg];
-                    zv[b][u][c] = W.zeros[b][sg];
-                } else {
-                    wv[b][u][c] = typename G::Chunk{};
-                    sv[b][u][c] = 0;
-                    zv[b][u][c] = 0;
-                }
-            }
-    }
-
-    // Activations for this lane's k positions, reused for every row.
-    f16x2 xr[CPR][PAIRS];
-    if constexpr (LN) {
-        constexpr int VPT = K / 256;  // values per thread
-        static_assert(VPT % 4 == 0, "K must be a multiple of 1024 for the fused LayerNorm");
-        __shared__ uint32_t xl[K / 2];
-        __shared__ float part[2][4];
-        const int t = threadIdx.x;
-        const int w = t >> 6;
-        float v[VPT];
-        const float4* hp = (const float4*)(hln + t * VPT);
-#pragma unroll
-        for (int i = 0; i < VPT / 4; ++i) {
-            const float4 q = hp[i];
-            v[4 * i] = q.x;
-            v[4 * i + 1] = q.y;
-            v[4 * i + 2] = q.z;
-            v[4 * i + 3] = q.w;
-        }
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) sum += v[i];
-        sum = segment_sum<64>(sum);
-        if (lane == 0) part[0][w] = sum;
-        __syncthreads();
-        const float mean = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) / (float)K;
-        float sq = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            v[i] -= mean;
-            sq += v[i] * v[i];
-        }
-        sq = segment_sum<64>(sq);
-        if (lane == 0) part[1][w] = sq;
-        __syncthreads();
-        const float var = ((part[1][0] + part[1][1]) + (part[1][2] + part[1][3])) / (float)K;
-        const float rstd = 1.0f / sqrtf(var + 1e-5f);
-#pragma unroll
-        for (int i = 0; i < VPT / 2; ++i)
-            xl[t * (VPT / 2) + i] =
-                as_u32(f16x2{(f16)(v[2 * i] * rstd), (f16)(v[2 * i + 1] * rstd)});
-        if (norm_out != nullptr && blockIdx.x == 0) {
-            uint32_t* op = (uint32_t*)norm_out + t * (VPT / 2);
-#pragma unroll
-            for (int i = 0; i < VPT / 2; ++i) op[i] = xl[t * (VPT / 2) + i];
-        }
-        __syncthreads();
-        if (!active) return;
-#pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const int p0 = (c * LPR + sub) * 16;
-#pragma unroll
-            for (int i = 0; i < PAIRS; ++i) xr[c][i] = as_f16x2(xl[p0 + i]);
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const int k0 = (c * LPR + sub) * 32;
-            const u32x4* xp = (const u32x4*)(X + k0);
-#pragma unroll
-            for (int v = 0; v < PAIRS / 4; ++v) {
-                const u32x4 t = xp[v];
-                xr[c][4 * v + 0] = as_f16x2(t.x);
-                xr[c][4 * v + 1] = as_f16x2(t.y);
-                xr[c][4 * v + 2] = as_f16x2(t.z);
-                xr[c][4 * v + 3] = as_f16x2(t.w);
-            }
-        }
-    }
-    float xs[CPR][G::NC], xs_all[CPR];
-#pragma unroll
-    for (int c = 0; c < CPR; ++c) {
-        G::xsums(xr[c], xs[c]);
-        xs_all[c] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < G::NC; ++j) xs_all[c] += xs[c][j];
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float acc[NW];
-#pragma unroll
-        for (int b = 0; b < NW; ++b) {
-            acc[b] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < CPR; ++c) {
-                float a[G::NC];
-#pragma unroll
-                for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
-                G::accumulate(wv[b][u][c], xr[c], a);
-                const float t = G::centred(a, xs[c], xs_all[c], (float)as_f16(zv[b][u][c]));
-                acc[b] += t * (float)as_f16(sv[b][u][c]);
-            }
-            acc[b] = segment_sum<LPR>(acc[b]);
-        }
-        const int row = row0 + u * RPW + rsub;
-        if (sub == 0 && row < N) {
-            if constexpr (NW == 1) {
-                epi_store(out, 0, row, acc[0]);
-            } else {
-                const uint16_t g16 = f32_to_f16_bits(acc[0]);
-                gout[row] = g16;
-                out.Y[row] = swiglu_f16(g16, f32_to_f16_bits(acc[1]));
-            }
-        }
-    }
-}
 
 // ------------------------------------------------------ MFMA B fragments ----
 
@@ -451,105 +199,6 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 
 // ------------------------------------------------------------ dispatch ----
 
-struct GemvShape {
-    int lpr, cpr;
-    bool ok;
-};
-
-GemvShape gemv_shape(int bits, int K) {
-    (void)bits;  // a lane chunk is 32 codes for both widths
-    const int chunks = K / 32;  // lane chunks per row
-    GemvShape s{0, 0, false};
-    if (chunks >= 64) {
-        if (chunks % 64) return s;
-        s.lpr = 64;
-        s.cpr = chunks / 64;
-        s.ok = s.cpr == 1 || s.cpr == 2 || s.cpr == 4 || s.cpr == 8;
-    } else {
-        s.lpr = chunks;
-        s.cpr = 1;
-        s.ok = chunks == 16 || chunks == 32;
-    }
-    return s;
-}
-
-// Rows per wave U: several rows per wave amortise the activations held in
-// registers (and the fused LayerNorm) but cut the number of waves in flight.
-// Measured on MI355X inside the looped block with its weights cache-resident
-// (D = 2048, F = 8192, M = 1): U = 2 from 2048 row steps (QKV, out, up, down,
-// the SwiGLU pair), else U = 1.  U = 4 on the 8192-step FFN projections was
-// even for INT4 and 2-6 % slower per iteration for INT2 and the SwiGLU pair;
-// U = 1 and U = 4 on the 2048-step ones were slower.  At most 8 outstanding
-// code loads per lane (U * CPR * NW <= 8, NW = 2 for the SwiGLU pair).
-template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
-hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
-    static_assert(U * CPR * NW <= 8, "at most 8 code loads per lane");
-    constexpr int RPW = 64 / LPR;
-    constexpr int kWavesPerBlock = 4;
-    const int N = a.w->N;
-    const int steps = (N + RPW - 1) / RPW;
-    const int waves = (steps + U - 1) / U;
-    const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    const qg_weight* w1 = NW == 2 ? a.w2 : a.w;
-    const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros},
-                        sz_idx(*a.w)};
-    k_gemv<BITS, LPR, CPR, U, LN, NW><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
-        a.X, a.ln_h, a.norm_out, W, N, a.out(), a.g_out);
-    return hipGetLastError();
-}
-
-// The fused LayerNorm needs K = 32*LPR*CPR to be a multiple of 1024 and
-// at most 8192 (the LN input is a residual row of D <= 8192 values).
-template <int BITS, int LPR, int CPR>
-constexpr bool ln_variant_ok() {
-    constexpr int K = 32 * LPR * CPR;
-    return K % 1024 == 0 && K <= 8192;
-}
-
-template <int BITS, int LPR, int CPR, bool LN>
-hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
-    if constexpr (LN && !ln_variant_ok<BITS, LPR, CPR>()) {
-        return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_layernorm
-    } else {
-    constexpr int RPW = 64 / LPR;
-    const int steps = (a.w->N + RPW - 1) / RPW;
-    if (a.w2 != nullptr) {  // SwiGLU pair: two weights per row step
-        if constexpr (CPR <= 4) {
-            if constexpr (CPR <= 2) {
-                if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 2>(a, s);
-            }
-            return launch_gemv_u<BITS, LPR, CPR, 1, LN, 2>(a, s);
-        } else {
-            return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_swiglu
-        }
-    }
-    if constexpr (CPR <= 4) {
-        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 1>(a, s);
-    }
-    return launch_gemv_u<BITS, LPR, CPR, 1, LN, 1>(a, s);
-    }
-}
-
-template <int BITS, bool LN>
-hipError_t launch_gemv_ln(const GemmArgs& a, hipStream_t s) {
-    const GemvShape g = gemv_shape(BITS, a.w->K);
-    if (g.lpr == 64) {
-        switch (g.cpr) {
-            case 1: return launch_gemv_t<BITS, 64, 1, LN>(a, s);
-            case 2: return launch_gemv_t<BITS, 64, 2, LN>(a, s);
-            case 4: return launch_gemv_t<BITS, 64, 4, LN>(a, s);
-            default: return launch_gemv_t<BITS, 64, 8, LN>(a, s);
-        }
-    }
-    if (g.lpr == 32) return launch_gemv_t<BITS, 32, 1, LN>(a, s);
-    return launch_gemv_t<BITS, 16, 1, LN>(a, s);
-}
-
-template <int BITS>
-hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
-    return a.ln_h ? launch_gemv_ln<BITS, true>(a, s) : launch_gemv_ln<BITS, false>(a, s);
-}
-
 // K parts of the skinny kernel: enough that each spans at most kSkinnyMaxK.
 int skinny_parts(int K) { return (K + kSkinnyMaxK - 1) / kSkinnyMaxK; }
 
@@ -575,7 +224,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 GemmPath gemm_path(int bits, int M, int K, int N) {
     (void)N;
-    if (M == 1 && gemv_shape(bits, K).ok) return kPathGemv;
+    if (M == 1 && gemv_supported(bits, K)) return kPathGemv;
     if (M <= 16 && K <= 4 * kSkinnyMaxK) return kPathSkinny;
     return kPathTiled;
 }
@@ -585,7 +234,7 @@ bool gemm_fuses_layernorm(int bits, int M, int K, int N) {
 }
 
 bool gemm_fuses_swiglu(int bits, int M, int K, int N) {
-    return gemm_path(bits, M, K, N) == kPathGemv && gemv_shape(bits, K).cpr <= 4;
+    return gemm_path(bits, M, K, N) == kPathGemv && gemv_pairs_supported(bits, K);
 }
 
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {
@@ -606,7 +255,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
                              a.w2->group == a.w->group))
         return hipErrorInvalidValue;
     switch (gemm_path(bits, a.M, a.w->K, a.w->N)) {
-        case kPathGemv: return bits == 4 ? launch_gemv<4>(a, s) : launch_gemv<2>(a, s);
+        case kPathGemv: return launch_gemv(a, s);
         case kPathSkinny: return bits == 4 ? launch_skinny<4>(a, s) : launch_skinny<2>(a, s);
         default: return launch_prefill(a, s);
     }
