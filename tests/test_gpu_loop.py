@@ -110,6 +110,7 @@ MEASURED = [
     ("c4a_int2_m1_l16", 2, 1, 16, [0]),
     ("c4b_int2_m128_l8", 2, 128, 8, [0, 77, 127]),
     ("c5a_int4_m16_l32", 4, 16, 32, [0, 15]),
+    ("medium_int4_m64_l8", 4, 64, 8, [0, 31, 63]),
 ]
 
 
@@ -202,7 +203,7 @@ def test_loop_gated_block(orc, bits, M, D, F):
     _check_scratch(qg.scratch_views(blk, M, scratch), last, rows, f"gated bits={bits} M={M}")
 
 
-@pytest.mark.parametrize("M,L", [(1, 8), (16, 4)])
+@pytest.mark.parametrize("M,L", [(1, 8), (16, 4), (512, 8)])
 def test_loop_gated_measured_block_sampled_rows(orc, M, L):
     """The pages' five-weight block at D=2048, F=8192 (INT4)."""
     D, F = workloads.D_MODEL, workloads.D_FFN

@@ -111,3 +111,19 @@ def test_perrow_loop_block(orc, bits, M, gated):
     rms = float(np.sqrt(np.mean(href ** 2)))
     assert_close(h.cpu().numpy(), href, f"per-row loop bits={bits} M={M} gated={gated}",
                  max_abs=1e-2 * max(1.0, rms))
+
+
+def test_perrow_measured_block_m1_l8(orc):
+    """The measured per-row workload at its real size: the D=2048, F=8192
+    INT4 block with one scale and zero per channel, M=1, L=8 (the bench's
+    launch configuration: fused-LayerNorm GEMVs through the cached graph)."""
+    D, F, L, M = workloads.D_MODEL, workloads.D_FFN, 8, 1
+    inp = workloads.block(M, seed=0, D=D, F=F)
+    blk = qg.pack_block(inp.W, 4, D, F, per_row=True)
+    oblk = orc.pack_block({k: v.numpy() for k, v in inp.W.items()}, 4, D, F, per_row=True)
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    href, _ = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
+    rms = float(np.sqrt(np.mean(href ** 2)))
+    assert_close(h.cpu().numpy(), href, "per-row measured block", max_abs=1e-2 * max(1.0, rms))
