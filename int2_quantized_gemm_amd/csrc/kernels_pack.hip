@@ -21,7 +21,8 @@ template <int BITS, bool PER_ROW>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64_t ldw, int K,
                                               int N, uint32_t* __restrict__ codes,
                                               uint16_t* __restrict__ scales,
-                                              uint16_t* __restrict__ zeros, int* status) {
+                                              uint16_t* __restrict__ zeros, int* status,
+                                              int tag) {
     using F = Fmt<BITS>;
     const int gl = PER_ROW ? K : kGroup;
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64
         }
         out[wi] = word;
     }
-    if (bad) atomicOr(status, 1);
+    if (bad) *status = tag;  // every failing thread stores the same call tag
 }
 
 // One thread per packed word: writes the word's codes q[n][k] as bytes.
@@ -120,18 +121,18 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
 }  // namespace
 
 hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
-                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status,
+                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status, int tag,
                        hipStream_t s) {
     dim3 grid((N + 255) / 256, K / group);
     const bool row = group != kGroup;
     if (bits == 4 && row)
-        k_pack<4, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<4, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else if (bits == 4)
-        k_pack<4, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<4, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else if (row)
-        k_pack<2, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<2, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else
-        k_pack<2, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status);
+        k_pack<2, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void k_requant_4to2(
     const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
-    int g0, int gcount, uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status) {
+    int g0, int gcount, uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status,
+    int tag) {
     const int groups = K / kGroup;
     // grid: x over the groups of a row (4 lanes each), y over the rows
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void k_requant_4to2(
         scales2[sg] = s_store;
         zeros2[sg] = f64_to_f16_bits(z2);
     }
-    if (bad) atomicOr(status, 1);
+    if (bad) *status = tag;  // every failing thread stores the same call tag
 }
 
 // Per-row groups: workgroup x covers row row0 + x; thread t takes
@@ -129,7 +130,7 @@ constexpr int kRowPairs = kRequantRowMaxK / 16 / 256;  // INT2 words per thread,
 
 __global__ __launch_bounds__(256) void k_requant_4to2_row(
     const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
-    uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status) {
+    uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status, int tag) {
     __shared__ int red[2][4];
     __shared__ uint32_t tab[16];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -205,14 +206,14 @@ __global__ __launch_bounds__(256) void k_requant_4to2_row(
     if (t == 0) {
         scales2[n] = s_store;
         zeros2[n] = f64_to_f16_bits(z2);
-        if (bad) atomicOr(status, 1);
+        if (bad) *status = tag;  // every failing thread stores the same call tag
     }
 }
 
 }  // namespace
 
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
-                               int* status, hipStream_t s) {
+                               int* status, int tag, hipStream_t s) {
     const int K = w4.K, N = w4.N, groups = K / kGroup;
     uint32_t* c2 = const_cast<uint32_t*>(w2.codes);
     uint16_t* s2 = const_cast<uint16_t*>(w2.scales);
@@ -223,13 +224,13 @@ hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in
         const int threads = lanes >= 256 ? 256 : (lanes + 63) / 64 * 64;
         const dim3 grid((unsigned)((lanes + threads - 1) / threads), (unsigned)rows);
         k_requant_4to2<<<grid, threads, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, row0, g0,
-                                                gcount, c2, s2, z2, status);
+                                                gcount, c2, s2, z2, status, tag);
         return hipGetLastError();
     };
     if (per_row(w4)) {
         auto rows = [&](int64_t row0, int64_t count) {
             k_requant_4to2_row<<<(unsigned)count, 256, 0, s>>>(w4.codes, w4.scales, w4.zeros, K,
-                                                               (int)row0, c2, s2, z2, status);
+                                                               (int)row0, c2, s2, z2, status, tag);
             return hipGetLastError();
         };
         if (!in_place) return rows(0, N);

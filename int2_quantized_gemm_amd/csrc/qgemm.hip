@@ -312,10 +312,58 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
     return hipGraphLaunch(exec, s);
 }
 
-// Per-device status word for qg_pack and qg_requant_4to2 (library-owned, freed by
-// qg_release_cache).
+// Per-device status word for qg_pack and qg_requant_4to2: a device int into
+// which a failing kernel stores the call's tag, and a pinned host int it is
+// copied back to (a copy into pageable memory goes through a staging buffer
+// and costs several times the copy).  Each call takes the next nonzero tag, so
+// the word needs no clearing launch: it reports a failure of this call only
+// when it holds this call's tag.  Library-owned, freed by qg_release_cache.
+struct StatusWord {
+    int* dev = nullptr;
+    int* host = nullptr;
+    int tag = 0;
+};
 std::mutex g_pack_mu;
-int* g_pack_status[64] = {nullptr};
+StatusWord g_pack_status[64];
+
+// Enqueues launch(status, tag) on s with the current device's status word
+// and a fresh tag, copies the word back and synchronises s; *bad is set when
+// the launch reported a failure.  Caller holds g_pack_mu.
+template <class Launch>
+int run_with_status(const char* fn, hipStream_t s, Launch&& launch, int* bad) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
+    StatusWord& w = g_pack_status[dev];
+    if (!w.dev) {
+        // a fresh word starts at 0, which is never a tag
+        if ((e = hipMalloc((void**)&w.dev, sizeof(int))) != hipSuccess) {
+            w.dev = nullptr;
+            return fail(QG_ENOMEM, "%s: cannot allocate the 4-byte status word (%s)", fn,
+                        hipGetErrorString(e));
+        }
+        if ((e = hipMemset(w.dev, 0, sizeof(int))) != hipSuccess) {
+            (void)hipFree(w.dev);
+            w.dev = nullptr;
+            return hip_fail(fn, e);
+        }
+        w.tag = 0;
+    }
+    if (!w.host && (e = hipHostMalloc((void**)&w.host, sizeof(int), hipHostMallocDefault)) !=
+                       hipSuccess) {
+        w.host = nullptr;
+        return fail(QG_ENOMEM, "%s: cannot allocate the pinned status word (%s)", fn,
+                    hipGetErrorString(e));
+    }
+    w.tag = w.tag == 0x7FFFFFFF ? 1 : w.tag + 1;
+    if ((e = launch(w.dev, w.tag)) != hipSuccess) return hip_fail(fn, e);
+    if ((e = hipMemcpyAsync(w.host, w.dev, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return hip_fail(fn, e);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(fn, e);
+    *bad = *w.host == w.tag;
+    return QG_OK;
+}
 
 }  // namespace
 
@@ -343,28 +391,13 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     if (!aligned(W, 4) || !aligned(codes, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
         return fail(QG_EINVAL, "%s: misaligned pointer", fn);
     hipStream_t s = (hipStream_t)stream;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
     std::lock_guard<std::mutex> lock(g_pack_mu);
-    if (!g_pack_status[dev]) {
-        e = hipMalloc((void**)&g_pack_status[dev], sizeof(int));
-        if (e != hipSuccess) {
-            g_pack_status[dev] = nullptr;
-            return fail(QG_ENOMEM, "%s: cannot allocate the 4-byte status word (%s)", fn,
-                        hipGetErrorString(e));
-        }
-    }
-    int* st = g_pack_status[dev];
-    if ((e = hipMemsetAsync(st, 0, sizeof(int), s)) != hipSuccess) return hip_fail(fn, e);
-    if ((e = qg::launch_pack(W, ldw, K, N, bits, group, codes, scales, zeros, st, s)) != hipSuccess)
-        return hip_fail(fn, e);
-    int host = 0;
-    if ((e = hipMemcpyAsync(&host, st, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
-        return hip_fail(fn, e);
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(fn, e);
-    if (host)
+    int bad = 0;
+    const int st = run_with_status(fn, s, [&](int* status, int tag) {
+        return qg::launch_pack(W, ldw, K, N, bits, group, codes, scales, zeros, status, tag, s);
+    }, &bad);
+    if (st) return st;
+    if (bad)
         return fail(QG_EINVAL, "%s: W holds a non-finite value or a group whose scale overflows "
                                "FP16", fn);
     return ok();
@@ -419,28 +452,13 @@ int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
     }
     const bool in_place = w2->codes == w4->codes;
     hipStream_t s = (hipStream_t)stream;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
     std::lock_guard<std::mutex> lock(g_pack_mu);
-    if (!g_pack_status[dev]) {
-        e = hipMalloc((void**)&g_pack_status[dev], sizeof(int));
-        if (e != hipSuccess) {
-            g_pack_status[dev] = nullptr;
-            return fail(QG_ENOMEM, "%s: cannot allocate the 4-byte status word (%s)", fn,
-                        hipGetErrorString(e));
-        }
-    }
-    int* stw = g_pack_status[dev];
-    if ((e = hipMemsetAsync(stw, 0, sizeof(int), s)) != hipSuccess) return hip_fail(fn, e);
-    if ((e = qg::launch_requant_4to2(*w4, *w2, in_place, stw, s)) != hipSuccess)
-        return hip_fail(fn, e);
-    int host = 0;
-    if ((e = hipMemcpyAsync(&host, stw, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
-        return hip_fail(fn, e);
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(fn, e);
-    if (host)
+    int bad = 0;
+    const int rc = run_with_status(fn, s, [&](int* status, int tag) {
+        return qg::launch_requant_4to2(*w4, *w2, in_place, status, tag, s);
+    }, &bad);
+    if (rc) return rc;
+    if (bad)
         return fail(QG_EINVAL, "%s: w4 holds a non-finite scale or zero, or a group whose INT2 "
                                "scale overflows FP16", fn);
     return ok();
@@ -554,16 +572,18 @@ void qg_release_cache(void) {
     }
     std::lock_guard<std::mutex> lock(g_pack_mu);
     bool any = false;
-    for (int* p : g_pack_status) any |= p != nullptr;
+    for (const StatusWord& w : g_pack_status) any |= w.dev != nullptr || w.host != nullptr;
     if (!any) return;
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (int d = 0; d < 64; ++d) {
-        if (g_pack_status[d]) {
+        StatusWord& w = g_pack_status[d];
+        if (w.dev || w.host) {
             (void)hipSetDevice(d);
             (void)hipDeviceSynchronize();
-            (void)hipFree(g_pack_status[d]);
-            g_pack_status[d] = nullptr;
+            if (w.dev) (void)hipFree(w.dev);
+            if (w.host) (void)hipHostFree(w.host);
+            w = StatusWord{};
         }
     }
     (void)hipSetDevice(cur);

@@ -70,6 +70,29 @@ def test_pack_rejects_non_finite_and_overflow(bad):
         qg.qg_pack(torch.from_numpy(W).cuda(), 4)
 
 
+def test_status_word_reports_each_call_alone(orc):
+    """Pack and re-quantisation share one status word per device that is
+    never cleared between calls: a failure must fail its own call only, and
+    consecutive failures must each be reported."""
+    good, _ = workloads.single_gemm(1, 256, 16, seed=5)
+    bad = good.clone()
+    bad[7, 3] = float("nan")
+    for _ in range(2):
+        with pytest.raises(qg.QGValueError):
+            qg.qg_pack(bad.cuda(), 4)
+        p = qg.qg_pack(good.cuda(), 4)
+    _assert_pack_equal(p, orc.pack(good.numpy(), 4))
+    broken = qg.qg_pack(good.cuda(), 4)
+    broken.scales.view(torch.int16)[3, 1] = 0x7C00  # +inf
+    with pytest.raises(qg.QGValueError):
+        qg.qg_requant_4to2(broken)
+    qg.qg_requant_4to2(p)
+    with pytest.raises(qg.QGValueError):
+        qg.qg_pack(bad.cuda(), 2)
+    qg.qg_release_cache()  # the word is freed and allocated again
+    _assert_pack_equal(qg.qg_pack(good.cuda(), 2), orc.pack(good.numpy(), 2))
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_unpack_and_dequant_bit_exact(orc, bits):
     W, _ = workloads.single_gemm(1, 1024, 96, seed=bits)
