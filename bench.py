@@ -14,6 +14,8 @@ bandwidth: steps * L * (packed block bytes: codes + scales + zeros) / wall
 time.
 
 The JSON line also carries
+  * step_distribution: p10 / p50 / p90 of single steps timed with HIP events
+    after the timed region;
   * roofline: the dominant kernel of the step (the FFN down-projection GEMV,
     K=8192, N=2048, the same kernel and grid as inside the loop) timed with
     HIP events on the stream it runs on, over a captured batch of
@@ -422,6 +424,21 @@ def main():
     block_bytes = blk.nbytes()
     value = args.steps * L_MAIN * block_bytes / el / 1e9
     log(f"main: {args.steps} steps in {el * 1e3:.2f} ms -> {value:.1f} GB/s effective")
+    # Per-step distribution (after the timed region, so it does not touch
+    # `value`): each of `steps` further steps bracketed by HIP events on the
+    # stream the loop runs on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        qg.qg_loop_range(blk, h, 0, L_MAIN, scratch)
+        b.record()
+    torch.cuda.synchronize()
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pct = lambda q: round(step_us[min(len(step_us) - 1, int(q * len(step_us)))], 2)
+    step_dist = {"unit": "us per step (L=8 iterations), HIP events", "n": len(step_us),
+                 "p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90)}
+    log(f"step distribution: {step_dist}")
 
     # ---- roofline: the dominant kernel of the step in its loop configuration
     # (down projection: u [1][F] FP16 -> [1][D], the GEMV kernel the loop runs)
@@ -460,6 +477,7 @@ def main():
                    "block_bytes": block_bytes,
                    "iterations_per_step": L_MAIN},
         "roofline": roofline,
+        "step_distribution": step_dist,
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
