@@ -198,21 +198,40 @@ def cpu_baseline(budget_s: float):
     h0 = inp.X.numpy().astype(np.float64)
     block_bytes = sum(p.codes.nbytes + p.scales.nbytes + p.zeros.nbytes
                       for p in (ob.qkv, ob.out, ob.up, ob.down))
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.loop_range(ob, h0, 0, L_MAIN)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    def run(seconds):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.loop_range(ob, h0, 0, L_MAIN)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return steps, el
+
+    cores = oracle.num_threads()
+    steps, el = run(budget_s)
+    # the same on one core, for about half the budget
+    oracle.set_num_threads(1)
+    try:
+        steps1, el1 = run(budget_s / 2)
+    finally:
+        oracle.set_num_threads(cores)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(steps * L_MAIN * block_bytes / el / 1e9, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{steps} whole steps of the same workload (INT4 block, M=1, L={L_MAIN}, "
                   f"seed 0) through the FP64 oracle, {el:.1f} s wall",
         "seconds": round(el, 2),
+        "single_core": {"value": round(steps1 * L_MAIN * block_bytes / el1 / 1e9, 4),
+                        "unit": "GB/s", "steps": steps1, "seconds": round(el1, 2)},
+        "cpu_model": model,
     }
 
 

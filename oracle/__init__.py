@@ -82,6 +82,8 @@ def lib():
             getattr(L, name).argtypes = [vp, i64, vp]
         L.or_num_threads.restype = C.c_int
         L.or_num_threads.argtypes = []
+        L.or_set_num_threads.restype = None
+        L.or_set_num_threads.argtypes = [C.c_int]
         L.or_half_bits_array.restype = None
         L.or_half_bits_array.argtypes = [vp, i64, vp]
         _lib = L
@@ -107,6 +109,11 @@ def _check(fn: str, st: int):
 def num_threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS or all cores)."""
     return lib().or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later oracle calls (timing only; results do not depend on it)."""
+    lib().or_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ FP16 ----

@@ -267,23 +267,26 @@ static int gemm_d(const double* X, int64_t ldx, int32_t M, const or_weight* w,
     int oom = 0;
 #pragma omp parallel reduction(| : oom)
     {
+        /* every thread of the team must reach the worksharing loop, also one
+         * whose buffer could not be allocated (it then skips its rows and the
+         * call reports OR_ENOMEM) */
         double* row = (double*)malloc(sizeof(double) * (size_t)K);
-        if (!row) {
+        if (!row)
             oom = 1;
-        } else {
 #pragma omp for schedule(static)
-            for (int32_t n = 0; n < N; ++n) {
-                dequant_row(w->codes, w->scales, w->zeros, K, w->bits, w->group, n, row);
-                for (int32_t m = 0; m < M; ++m) {
-                    const double* x = X + (int64_t)m * ldx;
-                    double acc = 0.0;
-                    for (int32_t k = 0; k < K; ++k)
-                        acc += x[k] * row[k];
-                    Y[(int64_t)m * ldy + n] = acc;
-                }
+        for (int32_t n = 0; n < N; ++n) {
+            if (!row)
+                continue;
+            dequant_row(w->codes, w->scales, w->zeros, K, w->bits, w->group, n, row);
+            for (int32_t m = 0; m < M; ++m) {
+                const double* x = X + (int64_t)m * ldx;
+                double acc = 0.0;
+                for (int32_t k = 0; k < K; ++k)
+                    acc += x[k] * row[k];
+                Y[(int64_t)m * ldy + n] = acc;
             }
-            free(row);
         }
+        free(row);
     }
     return oom ? OR_ENOMEM : OR_OK;
 }
@@ -468,4 +471,12 @@ void or_half_to_double_array(const uint16_t* h, int64_t n, double* out)
 int or_num_threads(void)
 {
     return omp_get_max_threads();
+}
+
+/* Sets the threads later OpenMP loops use (n >= 1); for timing the oracle on
+ * one core as well as on all of them.  Results do not depend on it: every
+ * parallel loop writes disjoint outputs and reduces only with a bitwise OR. */
+void or_set_num_threads(int n)
+{
+    omp_set_num_threads(n >= 1 ? n : 1);
 }
