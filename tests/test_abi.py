@@ -202,3 +202,25 @@ def test_requant_per_row_k_limit():
     w2 = _w(bits=2, K=K, N=4, group=K, codes=_C2, scales=_S2, zeros=_Z2)
     assert _rq(w4, w2) == qg.QG_EUNSUPPORTED
     assert "per-row" in qg.qg_last_error()
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: a copy of the package whose libqgemm.so is absent must
+    refuse to import (in a fresh interpreter, so this process's loaded
+    library is not reused)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "int2_quantized_gemm_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "int2_quantized_gemm_amd", "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n"
+            "    import int2_quantized_gemm_amd\n"
+            "except ImportError as e:\n"
+            "    print('IMPORT-ERROR', e)\n"
+            "else:\n"
+            "    print('IMPORTED', int2_quantized_gemm_amd.LIB_PATH)\n")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True,
+                       timeout=300)
+    assert "IMPORT-ERROR" in r.stdout and "no fallback" in r.stdout, r.stdout + r.stderr
