@@ -33,7 +33,6 @@ struct LaneCodes<4> {
     __device__ __forceinline__ void load(const uint32_t* row, int g, int c) {
         w = *(const u32x4*)(row + g * 16 + c * 4);
     }
-    __device__ __forceinline__ void zero() { w = u32x4{0, 0, 0, 0}; }
     // FP16 B fragment of MFMA step j: codes 8j..8j+7 of the lane = word j.
     __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc) const {
         const uint32_t x = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
@@ -48,7 +47,6 @@ struct LaneCodes<2> {
     __device__ __forceinline__ void load(const uint32_t* row, int g, int c) {
         w = *(const u32x2*)(row + g * 8 + c * 2);
     }
-    __device__ __forceinline__ void zero() { w = u32x2{0, 0}; }
     // Step j: codes 8j..8j+7 = pairs 4(j&1)..4(j&1)+3 of word j>>1.
     __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc) const {
         const uint32_t x = (j >> 1) ? w.y : w.x;
@@ -61,19 +59,6 @@ struct LaneCodes<2> {
 
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// A fragments of one 128-k group for one lane: X[m][g*128 + 32c + 8j .. +8].
-__device__ __forceinline__ void load_a(const uint16_t* xrow, bool valid, int g, int c, f16x8 a[4]) {
-    if (valid) {
-        const f16x8* p = (const f16x8*)(xrow + g * kGroup + c * 32);
-        a[0] = p[0];
-        a[1] = p[1];
-        a[2] = p[2];
-        a[3] = p[3];
-    } else {
-        a[0] = a[1] = a[2] = a[3] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
 }
 
 // ---------------------------------------------------------------- skinny ----
