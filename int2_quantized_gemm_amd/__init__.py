@@ -124,6 +124,18 @@ class PackedWeight:
     group: int = GROUP
 
     def cstruct(self) -> _Weight:
+        # the C side sees only pointers: the tensors must hold what bits, K,
+        # N and group say
+        if (tuple(self.codes.shape) != (self.N, self.K * self.bits // 32)
+                or self.codes.element_size() != 4 or not self.codes.is_contiguous()):
+            raise ValueError(f"codes must be a contiguous 32-bit [{self.N}][{self.K * self.bits // 32}]"
+                             f" tensor, got {tuple(self.codes.shape)} {self.codes.dtype}")
+        groups = self.K // self.group if self.group else 0
+        for name, t in (("scales", self.scales), ("zeros", self.zeros)):
+            if (tuple(t.shape) != (self.N, groups) or t.dtype != torch.float16
+                    or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous FP16 [{self.N}][{groups}] tensor, "
+                                 f"got {tuple(t.shape)} {t.dtype}")
         return _Weight(self.bits, self.K, self.N, self.group, self.codes.data_ptr(),
                        self.scales.data_ptr(), self.zeros.data_ptr())
 
@@ -162,9 +174,13 @@ def qg_gemm_ws_bytes(w: PackedWeight, M: int) -> int:
 
 
 def _gemm(fn, name, X, w, Y, ws, stream):
+    if X.dim() != 2 or X.shape[1] != w.K:
+        raise ValueError(f"X must be [M][{w.K}], got {tuple(X.shape)}")
     M = X.shape[0]
     if Y is None:
         Y = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if Y.dim() != 2 or tuple(Y.shape) != (M, w.N):
+        raise ValueError(f"Y must be [{M}][{w.N}], got {tuple(Y.shape)}")
     if X.dtype != torch.float16 or Y.dtype != torch.float16 or X.stride(1) != 1 or Y.stride(1) != 1:
         raise ValueError("X and Y must be row-major FP16 tensors")
     need = qg_gemm_ws_bytes(w, M)
@@ -185,6 +201,7 @@ def qg_gemm_int4(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None
 
 def qg_gemm_int2(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None, ws=None,
                  stream=None) -> torch.Tensor:
+    """Y[M][N] = X[M][K] . dequant(w) for 2-bit w, FP16 in/out, FP32 accumulation."""
     return _gemm(lib.qg_gemm_int2, "qg_gemm_int2", X, w, Y, ws, stream)
 
 
@@ -249,8 +266,9 @@ def scratch_views(blk: Block, M: int, scratch: torch.Tensor) -> dict:
 def qg_loop_range(blk: Block, h: torch.Tensor, L0: int, L1: int,
                   scratch: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Apply iterations [L0, L1) of the block in place on FP32 h [M][D]."""
-    if h.dtype != torch.float32 or not h.is_contiguous():
-        raise ValueError("h must be a contiguous FP32 [M][D] tensor")
+    if h.dtype != torch.float32 or not h.is_contiguous() or h.dim() != 2 or h.shape[1] != blk.D:
+        raise ValueError(f"h must be a contiguous FP32 [M][{blk.D}] tensor, got "
+                         f"{tuple(h.shape)} {h.dtype}")
     M = h.shape[0]
     if scratch is None:
         scratch = alloc_loop_scratch(blk, M, h.device)

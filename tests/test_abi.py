@@ -157,6 +157,32 @@ def test_python_binding_rejects_host_tensors():
         qg.qg_pack(torch.zeros(128, 8), 4)
 
 
+def test_python_binding_checks_shapes():
+    """The C side sees pointers and leading dimensions only, so the binding
+    checks the tensors' logical shapes before any call (CPU tensors: the
+    shape checks come first)."""
+    import torch
+    w = qg.PackedWeight(4, 256, 16, torch.zeros(16, 32, dtype=torch.int32),
+                        torch.zeros(16, 2, dtype=torch.float16),
+                        torch.zeros(16, 2, dtype=torch.float16))
+    X = torch.zeros(3, 256, dtype=torch.float16)
+    with pytest.raises(ValueError, match="X must be"):
+        qg.qg_gemm_int4(torch.zeros(3, 128, dtype=torch.float16), w)
+    with pytest.raises(ValueError, match="Y must be"):
+        qg.qg_gemm_int4(X, w, Y=torch.zeros(3, 8, dtype=torch.float16))
+    bad_codes = qg.PackedWeight(4, 256, 16, torch.zeros(16, 16, dtype=torch.int32), w.scales,
+                                w.zeros)
+    with pytest.raises(ValueError, match="codes must be"):
+        qg.qg_gemm_ws_bytes(bad_codes, 3)
+    bad_scales = qg.PackedWeight(4, 256, 16, w.codes, torch.zeros(16, 1, dtype=torch.float16),
+                                 w.zeros)
+    with pytest.raises(ValueError, match="scales must be"):
+        qg.qg_gemm_ws_bytes(bad_scales, 3)
+    blk = qg.Block(256, 512, *(w,) * 4)
+    with pytest.raises(ValueError, match="h must be"):
+        qg.qg_loop_range(blk, torch.zeros(2, 128, dtype=torch.float32), 0, 1)
+
+
 def test_product_does_not_reference_the_oracle():
     pkg = os.path.join(ROOT, "int2_quantized_gemm_amd")
     for dirpath, _, files in os.walk(pkg):
