@@ -172,10 +172,10 @@ int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t
 int qg_unpack(const qg_weight* w, uint8_t* q, void* stream);
 int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream);
 
-/* Frees library-owned state (cached launch plans; the device and pinned host
- * status words of qg_pack and qg_requant_4to2) after synchronising the
- * device.  Safe to call at any time when no library call is in flight on
- * another thread. */
+/* Frees library-owned state (cached loop graphs and their capture streams;
+ * the device and pinned host status words of qg_pack and qg_requant_4to2)
+ * after synchronising every device that holds some of it.  Safe to call at
+ * any time when no library call is in flight on another thread. */
 void qg_release_cache(void);
 
 #ifdef __cplusplus

@@ -257,6 +257,16 @@ uint64_t g_graph_clock = 0;
 hipStream_t g_capture_stream[64] = {nullptr};
 constexpr size_t kMaxGraphs = 32;
 
+// Waits for all work on `device` (a launch of a cached graph may still be
+// running there) and restores the caller's current device.
+void sync_device(int device) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    if (cur != device) (void)hipSetDevice(device);
+    (void)hipDeviceSynchronize();
+    if (cur != device) (void)hipSetDevice(cur);
+}
+
 // Launches the cached graph for these arguments on stream s, capturing and
 // instantiating it first if needed.  The launch happens under the cache lock,
 // so no other thread can evict (destroy) the graph between lookup and launch.
@@ -299,12 +309,12 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return e;
     if (g_graphs.size() >= kMaxGraphs) {
-        // Evict the least recently used graph; a graph already launched on a
-        // stream stays valid until that launch completes, so sync first.
+        // Evict the least recently used graph; a launch of it may still be
+        // running on its device, so wait for that device first.
         size_t lru = 0;
         for (size_t i = 1; i < g_graphs.size(); ++i)
             if (g_graphs[i].last_use < g_graphs[lru].last_use) lru = i;
-        (void)hipDeviceSynchronize();
+        sync_device(g_graphs[lru].key.device);
         (void)hipGraphExecDestroy(g_graphs[lru].exec);
         g_graphs.erase(g_graphs.begin() + lru);
     }
@@ -564,11 +574,25 @@ int qg_dequant(const qg_weight* w, int32_t out_fp16, void* out, void* stream) {
 void qg_release_cache(void) {
     {
         std::lock_guard<std::mutex> glock(g_graph_mu);
-        if (!g_graphs.empty()) {
-            (void)hipDeviceSynchronize();
-            for (LoopGraph& g : g_graphs) (void)hipGraphExecDestroy(g.exec);
-            g_graphs.clear();
+        bool synced[64] = {false};
+        for (LoopGraph& g : g_graphs) {
+            if (!synced[g.key.device]) {
+                sync_device(g.key.device);
+                synced[g.key.device] = true;
+            }
+            (void)hipGraphExecDestroy(g.exec);
         }
+        g_graphs.clear();
+        // the per-device capture streams (they only ever record, never run)
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        for (int d = 0; d < 64; ++d) {
+            if (!g_capture_stream[d]) continue;
+            (void)hipSetDevice(d);
+            (void)hipStreamDestroy(g_capture_stream[d]);
+            g_capture_stream[d] = nullptr;
+        }
+        (void)hipSetDevice(cur);
     }
     std::lock_guard<std::mutex> lock(g_pack_mu);
     bool any = false;

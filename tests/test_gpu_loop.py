@@ -316,3 +316,22 @@ def test_loop_graph_cache_from_threads(orc, monkeypatch):
     assert not errors, errors
     for i, h in enumerate(hs):
         assert torch.equal(h, ref), f"call {i}"
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_loop_after_release_cache(orc, M):
+    """qg_release_cache frees the cached graphs and their capture streams; the
+    next call captures again and gives the same bits (twice in a row, so a
+    release with nothing cached is harmless too)."""
+    D, F = 256, 640
+    inp, blk, _ = _blocks(orc, M, 4, D, F, seed=31)
+    h0 = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    first = h0.clone()
+    qg.qg_loop_range(blk, first, 0, 3, scratch)
+    for _ in range(2):
+        qg.qg_release_cache()
+        again = h0.clone()
+        qg.qg_loop_range(blk, again, 0, 3, scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
