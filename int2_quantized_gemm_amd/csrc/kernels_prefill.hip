@@ -629,14 +629,38 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     }
 }
 
-// Sum of the K-split partial tiles part[0..S)[M][N] in split order, then the
-// output epilogue.  Four elements per thread.
+// Sum of the K-split partial tiles part[0..S)[M][N] in split order
+// (((p0 + p1) + p2) + ...), then the output epilogue.  Four consecutive
+// elements per thread.  With N % 4 == 0 they share a row: one 16-byte load
+// per part, the loads of up to 8 parts issued before the first add, and one
+// row/column split per thread (these launches are latency-bound, so the
+// per-element scalar loads and 64-bit divisions of the general path cost
+// several microseconds at the loop block's shapes).
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
                                                        int M, int N, OutEpi out) {
     const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     const int64_t total = (int64_t)M * N;
     if (i4 >= total) return;
     const int64_t plane = total;
+    if ((N & 3) == 0) {
+        const int m = total <= 0x7FFFFFFF ? (int)((uint32_t)i4 / (uint32_t)N) : (int)(i4 / N);
+        const int n = (int)(i4 - (int64_t)m * N);
+        const f32x4* p = (const f32x4*)(part + i4);
+        const int64_t pl4 = plane / 4;
+        f32x4 acc = p[0];
+        for (int z0 = 1; z0 < S; z0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (z0 + j < S) v[j] = p[(z0 + j) * pl4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (z0 + j < S) acc += v[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) epi_store(out, m, n + e, acc[e]);
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t i = i4 + e;
