@@ -335,3 +335,19 @@ def test_loop_after_release_cache(orc, M):
         qg.qg_loop_range(blk, again, 0, 3, scratch)
         torch.cuda.synchronize()
         assert torch.equal(first, again)
+
+
+@pytest.mark.parametrize("D,F", [(1024, 256), (2048, 256), (4096, 384), (8192, 256), (384, 256)])
+def test_loop_layernorm_widths(orc, D, F):
+    """The LayerNorm kernel of M > 1 at every row width it has a vectorised
+    variant for (D = 1024 .. 8192) and at an element-strided one (D = 384):
+    the block at M = 3 against the oracle, h and the last iteration's scratch
+    (its norm is the LayerNorm kernel's output)."""
+    M, L = 3, 2
+    inp, blk, oblk = _blocks(orc, M, 4, D, F, seed=D + F)
+    h = inp.X.float().cuda()
+    scratch = qg.alloc_loop_scratch(blk, M)
+    qg.qg_loop_range(blk, h, 0, L, scratch)
+    href, last = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
+    _check_h(h.cpu().numpy(), href, f"LN width D={D}")
+    _check_scratch(qg.scratch_views(blk, M, scratch), last, list(range(M)), f"LN width D={D}")
