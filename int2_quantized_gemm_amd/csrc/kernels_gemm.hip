@@ -66,7 +66,8 @@ __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f3
 // 2 <= M <= 16.  A workgroup of four waves computes NT tiles of 16 output
 // channels over one K part (at most kSkinnyMaxK values; K is cut into S
 // parts, summed by k_splitk_reduce when S > 1).  The activation rows of the part are staged
-// once in LDS -- 16 rows (rows past M are zero or unused) of R values,
+// once in LDS -- the M rows of R values (LDS rows M..15 hold stale data that
+// only reaches accumulator rows that are never stored),
 // 16-byte chunk ci of row m at chunk slot ci ^ (m % 16), so the fragment
 // reads of the 16 rows hit distinct banks -- by LDS DMA of contiguous row
 // pieces; the MFMA A fragments then come from LDS instead of 16-byte pieces of
@@ -126,9 +127,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         }
     }
 
-    // the part's activation rows, 1 KiB per DMA instruction
+    // the part's M activation rows, 1 KiB per DMA instruction.  LDS rows
+    // M..15 are left as they are: MFMA rows do not mix, so they only reach
+    // accumulator rows >= M, which are never stored.
     const i32x4 rx = make_rsrc_sgpr(X, ((int64_t)(M - 1) * ldx + K) * 2);
-    const int units = 16 * cpr;
+    const int units = M * cpr;
     for (int u0 = wave * 64; u0 < units; u0 += 256) {
         const int u = u0 + lane;
         const int row = u / cpr, slot = u % cpr;
