@@ -66,6 +66,22 @@ def test_gemm_block_shapes(orc, bits, M, K, N):
     assert_close(Y, ref, f"bits={bits} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M", [1, 3, 33])
+def test_gemm_maximum_k(orc, bits, M):
+    """K at the ABI's limit (2^22): no GEMV lane arrangement covers it, so even
+    M = 1 runs the tiled kernel with its K split; N ragged (24).  The outputs
+    (std ~ 0.02 sqrt(K) ~ 41) are far above the configs' |Y| < 10, where one
+    FP16 step of the required output rounding exceeds 1e-2: max-abs is
+    therefore two FP16 steps at the largest reference value (rel-L2 stays
+    2e-3)."""
+    K, N = 1 << 22, 24
+    Y, ref = _case(orc, bits, M, K, N, seed=M + bits)
+    top = float(np.max(np.abs(ref)))
+    ulp = 2.0 ** (np.floor(np.log2(max(top, 2.0 ** -14))) - 10)
+    assert_close(Y, ref, f"max K bits={bits} M={M}", max_abs=max(1e-2, 2 * ulp))
+
+
 def test_gemm_c1_seed0(orc):
     """Single INT4 GEMM, M=1, K=N=2048, seed 0 -- the single-pass workload."""
     Y, ref = _case(orc, 4, 1, 2048, 2048, seed=0)
