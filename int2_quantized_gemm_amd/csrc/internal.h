@@ -60,6 +60,10 @@ struct GemmArgs {
     // kStore.
     const qg_weight* w2 = nullptr;
     qg_half* g_out = nullptr;
+    // Parts mode (M > 1 only): the GEMM writes its FP32 K-part partials
+    // ws[0..S)[M][N] (S >= 1, also when it would not split) and no output;
+    // *parts receives S.  The caller finishes with launch_reduce_residual_ln.
+    int* parts = nullptr;
 
     OutEpi out() const { return OutEpi{Y, ldy, h, ldh, gm, ldg, (int)epi}; }
 };
@@ -85,6 +89,8 @@ bool gemm_fuses_swiglu(int bits, int M, int K, int N);
 enum GemmPath { kPathGemv = 0, kPathSkinny = 1, kPathTiled = 2 };
 GemmPath gemm_path(int bits, int M, int K, int N);
 size_t gemm_ws_bytes(int bits, int M, int K, int N);
+// Workspace a parts-mode launch of this shape needs (its partials).
+size_t gemm_parts_ws_bytes(int bits, int M, int K, int N);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // M > 16 (and M <= 16 with K > 8192): the tiled MFMA GEMMs of
 // kernels_prefill.hip (ring kernel with 32-, 64- or 128-row tiles, or the
@@ -99,5 +105,13 @@ size_t prefill_ws_bytes(int M, int N, int K);
 // ---- loop glue (kernels_loop.hip)
 // norm[m][:] = fp16(LN(h[m][:])), parameter-free, eps 1e-5, FP32.
 hipError_t launch_layernorm(const float* h, int M, int D, qg_half* norm, hipStream_t s);
+// A residual projection's end and the following LayerNorm in one launch:
+// y = fp16(sum of part[0..S)[M][D] in part order) to Y [M][D], h += y, and
+// norm = fp16(LN(h)) unless norm is NULL.  Bit-identical to the split-K
+// reduction with the residual epilogue followed by launch_layernorm.  For
+// the D that reduce_ln_supported accepts.
+bool reduce_ln_supported(int D);
+hipError_t launch_reduce_residual_ln(const float* part, int S, int M, int D, qg_half* Y, float* h,
+                                     qg_half* norm, hipStream_t s);
 
 }  // namespace qg

@@ -193,7 +193,7 @@ int skinny_parts(int K) { return (K + kSkinnyMaxK - 1) / kSkinnyMaxK; }
 template <int BITS>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     const int S = skinny_parts(a.w->K);
-    float* part = S > 1 ? (float*)a.ws : nullptr;
+    float* part = S > 1 || a.parts ? (float*)a.ws : nullptr;
     const int pairs = (a.w->N + 31) / 32;
     if ((int64_t)pairs * S >= kSkinnyPairMinWgs)
         k_gemm_skinny<BITS, 2><<<dim3(pairs, S), 256, 0, s>>>(
@@ -204,7 +204,8 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
             a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N, S,
             a.out(), part);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || S == 1) return e;
+    if (a.parts) *a.parts = S;
+    if (e != hipSuccess || S == 1 || a.parts) return e;
     return launch_splitk_reduce(part, S, a, s);
 }
 
@@ -225,6 +226,17 @@ bool gemm_fuses_swiglu(int bits, int M, int K, int N) {
     return gemm_path(bits, M, K, N) == kPathGemv && gemv_pairs_supported(bits, K);
 }
 
+size_t gemm_parts_ws_bytes(int bits, int M, int K, int N) {
+    switch (gemm_path(bits, M, K, N)) {
+        case kPathSkinny: return (size_t)skinny_parts(K) * M * N * sizeof(float);
+        case kPathTiled: {
+            const size_t split = prefill_ws_bytes(M, N, K);
+            return split > 0 ? split : (size_t)M * N * sizeof(float);
+        }
+        default: return 0;
+    }
+}
+
 size_t gemm_ws_bytes(int bits, int M, int K, int N) {
     switch (gemm_path(bits, M, K, N)) {
         case kPathSkinny: {
@@ -242,7 +254,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
                              a.w2->bits == bits && a.w2->K == a.w->K && a.w2->N == a.w->N &&
                              a.w2->group == a.w->group))
         return hipErrorInvalidValue;
-    switch (gemm_path(bits, a.M, a.w->K, a.w->N)) {
+    const GemmPath path = gemm_path(bits, a.M, a.w->K, a.w->N);
+    if (a.parts != nullptr && (path == kPathGemv || a.w2 != nullptr))
+        return hipErrorInvalidValue;  // parts mode is for the MFMA kernels
+    switch (path) {
         case kPathGemv: return launch_gemv(a, s);
         case kPathSkinny: return bits == 4 ? launch_skinny<4>(a, s) : launch_skinny<2>(a, s);
         default: return launch_prefill(a, s);

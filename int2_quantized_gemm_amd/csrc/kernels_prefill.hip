@@ -766,12 +766,13 @@ template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int ST
 hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     dim3 grid((a.w->N + BN - 1) / BN, (a.M + BM - 1) / BM, split);
     constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
-    float* part = split > 1 ? (float*)a.ws : nullptr;
+    float* part = split > 1 || a.parts ? (float*)a.ws : nullptr;
     k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
         a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N,
         a.out(), a.w->K / kBK / split, part);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || split == 1) return e;
+    if (a.parts) *a.parts = split;
+    if (e != hipSuccess || split == 1 || a.parts) return e;
     return reduce_parts(a, split, part, s);
 }
 
@@ -782,12 +783,13 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const double b_bytes = 128.0 * a.w->K * BITS / 8 / split;
     const Raster rs = make_raster(gx, gy, a_bytes, b_bytes);
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
-    float* part = split > 1 ? (float*)a.ws : nullptr;
+    float* part = split > 1 || a.parts ? (float*)a.ws : nullptr;
     k_gemm_ring<BITS, BM, RA, RBS, SZ><<<grid, 256, 0, s>>>(
         a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
         a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || split == 1) return e;
+    if (a.parts) *a.parts = split;
+    if (e != hipSuccess || split == 1 || a.parts) return e;
     return reduce_parts(a, split, part, s);
 }
 

@@ -121,7 +121,13 @@ LoopLayout loop_layout(const qg_block* b, int32_t M) {
     const qg_weight* ws_list[5] = {&b->qkv, &b->out, &b->up, &b->down, &b->gate};
     for (const qg_weight* w : ws_list) {
         if (w == &b->gate && !gated(b)) continue;
-        const size_t n = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
+        size_t n = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
+        // the residual projections' partials when their end is fused with
+        // the next LayerNorm (M > 1)
+        if (M > 1 && (w == &b->out || w == &b->down) && qg::reduce_ln_supported(b->D)) {
+            const size_t p = qg::gemm_parts_ws_bytes(w->bits, M, w->K, w->N);
+            n = p > n ? p : n;
+        }
         ws = n > ws ? n : ws;
     }
     L.ws_bytes = ws;
@@ -164,9 +170,17 @@ bool swiglu_fusion_enabled() {
     return !(v && v[0] == '0');
 }
 
+// QG_FUSE_REDUCE_LN=0 keeps the residual projections' split-K reduction and
+// the following LayerNorm as separate launches at M > 1 (the fused-versus-
+// separate parity test); read on every call.
+bool reduce_ln_fusion_enabled() {
+    const char* v = getenv("QG_FUSE_REDUCE_LN");
+    return !(v && v[0] == '0');
+}
+
 // Enqueue `iters` iterations of the loop block on stream s (no validation).
 hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
-                        const LoopLayout& L, bool fuse_swiglu, hipStream_t s) {
+                        const LoopLayout& L, bool fuse_swiglu, bool fuse_rln, hipStream_t s) {
     char* base = (char*)scratch;
     qg_half* norm = (qg_half*)(base + L.norm);
     qg_half* qkv = (qg_half*)(base + L.qkv);
@@ -185,14 +199,32 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     const bool pair = gate && fuse_swiglu && blk->gate.bits == blk->up.bits &&
                       blk->gate.group == blk->up.group &&
                       qg::gemm_fuses_swiglu(blk->up.bits, M, D, F);
+    // At M > 1 each residual projection (out, down) writes its K-part
+    // partials and one launch sums them, adds the result into h and computes
+    // the LayerNorm that follows (of the FFN input after out, of the next
+    // iteration's QKV input after down; not after the last down, so that norm
+    // keeps the last FFN input).  Bit-identical to the separate launches.
+    const bool rln = fuse_rln && M > 1 && qg::reduce_ln_supported(D);
+    // A residual projection with its end fused: partials, then one launch.
+    auto residual_ln = [&](const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* ln_out) {
+        int parts = 0;
+        qg::GemmArgs ra{X, ldx, w, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes};
+        ra.parts = &parts;
+        hipError_t r = qg::launch_gemm(ra, s);
+        if (r == hipSuccess)
+            r = qg::launch_reduce_residual_ln((const float*)ws, parts, M, D, y, h, ln_out, s);
+        return r;
+    };
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
         qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
         if (fuse_qkv)
             qa.ln_h = h;
-        else
+        else if (!(rln && l > 0))  // (else the previous down's launch wrote norm)
             e = qg::launch_layernorm(h, M, D, norm, s);
         if (e == hipSuccess) e = qg::launch_gemm(qa, s);
-        if (e == hipSuccess)
+        if (e == hipSuccess && rln)
+            e = residual_ln(qkv + 2 * D, 3 * D, &blk->out, norm);
+        else if (e == hipSuccess)
             e = qg::launch_gemm({qkv + 2 * D, 3 * D, &blk->out, y, D, M, qg::kResidual, h, D, ws,
                                  L.ws_bytes},
                                 s);
@@ -205,7 +237,7 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
         if (fuse_first) {
             fa.ln_h = h;
             fa.norm_out = norm;
-        } else if (e == hipSuccess) {
+        } else if (e == hipSuccess && !rln) {
             e = qg::launch_layernorm(h, M, D, norm, s);
         }
         if (pair) {
@@ -220,7 +252,9 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
             ua.ldg = F;
             e = qg::launch_gemm(ua, s);
         }
-        if (e == hipSuccess)
+        if (e == hipSuccess && rln)
+            e = residual_ln(u, F, &blk->down, l + 1 < iters ? norm : nullptr);
+        else if (e == hipSuccess)
             e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
                                 s);
     }
@@ -241,7 +275,7 @@ struct LoopKey {
     const float* h;
     void* scratch;
     int32_t M, iters, device;
-    bool fuse_swiglu;
+    bool fuse_swiglu, fuse_rln;
     bool operator==(const LoopKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
 };
 
@@ -271,7 +305,7 @@ void sync_device(int device) {
 // instantiating it first if needed.  The launch happens under the cache lock,
 // so no other thread can evict (destroy) the graph between lookup and launch.
 hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters,
-                             void* scratch, const LoopLayout& L, bool fuse_swiglu,
+                             void* scratch, const LoopLayout& L, bool fuse_swiglu, bool fuse_rln,
                              hipStream_t s) {
     LoopKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
@@ -281,6 +315,7 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
     key.M = M;
     key.iters = iters;
     key.fuse_swiglu = fuse_swiglu;
+    key.fuse_rln = fuse_rln;
     hipError_t e = hipGetDevice(&key.device);
     if (e != hipSuccess) return e;
     if (key.device < 0 || key.device >= 64) return hipErrorInvalidDevice;
@@ -297,7 +332,7 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
         return e;
     }
     if ((e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
-    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, cs);
+    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, fuse_rln, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {
@@ -544,10 +579,11 @@ int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t 
     // kernels are enqueued one by one; otherwise the iteration sequence is
     // replayed from a cached graph (one launch instead of 4-6 per iteration).
     const bool fuse_swiglu = swiglu_fusion_enabled();
+    const bool fuse_rln = reduce_ln_fusion_enabled();
     if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled()) {
-        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, s);
+        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, fuse_rln, s);
     } else {
-        e = launch_loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, s);
+        e = launch_loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, fuse_rln, s);
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();

@@ -351,3 +351,31 @@ def test_loop_layernorm_widths(orc, D, F):
     href, last = orc.loop_range(oblk, inp.X.numpy().astype(np.float64), 0, L)
     _check_h(h.cpu().numpy(), href, f"LN width D={D}")
     _check_scratch(qg.scratch_views(blk, M, scratch), last, list(range(M)), f"LN width D={D}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,D,F,gated", [(2, 1024, 2304, False), (16, 2048, 8192, False),
+                                         (16, 1024, 4096, True), (33, 1024, 1152, False),
+                                         (64, 2048, 8192, False), (128, 1024, 2048, True),
+                                         (300, 2048, 1024, False), (5, 4096, 512, False),
+                                         (3, 8192, 256, False)])
+def test_loop_fused_residual_layernorm_matches_separate_launches(orc, monkeypatch, bits, M, D, F,
+                                                                 gated):
+    """At M > 1 the residual projections write K-part partials and one launch
+    sums them, adds into h and computes the next LayerNorm.  It must give the
+    same bits as the split-K reduction (or the GEMM's own epilogue) followed
+    by the LayerNorm kernel (QG_FUSE_REDUCE_LN=0): h and every scratch region,
+    over several iterations (skinny with and without K parts, ring tiles with
+    and without a K split, INT4 and INT2, plain and gated)."""
+    inp, blk, _ = _blocks(orc, M, bits, D, F, seed=M + D + F + bits, gated=gated)
+    scratch = qg.alloc_loop_scratch(blk, M)
+    out = {}
+    for fuse in ("0", "1"):
+        monkeypatch.setenv("QG_FUSE_REDUCE_LN", fuse)
+        h = inp.X.float().cuda()
+        qg.qg_loop_range(blk, h, 0, 3, scratch)
+        torch.cuda.synchronize()
+        out[fuse] = (h.clone(), {k: v.clone() for k, v in qg.scratch_views(blk, M, scratch).items()})
+    assert torch.equal(out["0"][0], out["1"][0])
+    for k in out["0"][1]:
+        assert torch.equal(out["0"][1][k], out["1"][1][k]), k
