@@ -683,8 +683,9 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 constexpr int kSmallM = 128;
 
 // Ring kernel with 32-row tiles: K split into the most parts (at most 8) that
-// keep at most 256 workgroups and at least 8 groups per part; {-1, 0} where
-// the parts would not suit the ring.
+// keep at most 256 workgroups and at least 8 groups per part (also in parts
+// mode: parts of 4 groups there were 1-2 % slower per loop iteration at
+// M = 64..128); {-1, 0} where the parts would not suit the ring.
 Plan plan_ring32(int M, int N, int groups) {
     const int t32 = ceil_div(M, 32) * ceil_div(N, 128);
     int sp = 1;

@@ -170,9 +170,10 @@ bool swiglu_fusion_enabled() {
     return !(v && v[0] == '0');
 }
 
-// QG_FUSE_REDUCE_LN=0 keeps the residual projections' split-K reduction and
-// the following LayerNorm as separate launches at M > 1 (the fused-versus-
-// separate parity test); read on every call.
+// QG_FUSE_REDUCE_LN=0 ends the residual projections at M > 1 with the split-K
+// reduction and the LayerNorm kernel as two launches over the same partials,
+// instead of one fused launch (the fused-versus-separate parity test); read on
+// every call.
 bool reduce_ln_fusion_enabled() {
     const char* v = getenv("QG_FUSE_REDUCE_LN");
     return !(v && v[0] == '0');
@@ -203,16 +204,21 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     // partials and one launch sums them, adds the result into h and computes
     // the LayerNorm that follows (of the FFN input after out, of the next
     // iteration's QKV input after down; not after the last down, so that norm
-    // keeps the last FFN input).  Bit-identical to the separate launches.
-    const bool rln = fuse_rln && M > 1 && qg::reduce_ln_supported(D);
-    // A residual projection with its end fused: partials, then one launch.
+    // keeps the last FFN input).  With fuse_rln off the same partials go
+    // through the split-K reduction and the LayerNorm kernel instead, with
+    // bit-identical results.
+    const bool rln = M > 1 && qg::reduce_ln_supported(D);
     auto residual_ln = [&](const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* ln_out) {
         int parts = 0;
         qg::GemmArgs ra{X, ldx, w, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes};
         ra.parts = &parts;
         hipError_t r = qg::launch_gemm(ra, s);
-        if (r == hipSuccess)
-            r = qg::launch_reduce_residual_ln((const float*)ws, parts, M, D, y, h, ln_out, s);
+        if (r != hipSuccess) return r;
+        if (fuse_rln)
+            return qg::launch_reduce_residual_ln((const float*)ws, parts, M, D, y, h, ln_out, s);
+        ra.parts = nullptr;
+        r = qg::launch_splitk_reduce((const float*)ws, parts, ra, s);
+        if (r == hipSuccess && ln_out) r = qg::launch_layernorm(h, M, D, ln_out, s);
         return r;
     };
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {

@@ -363,9 +363,9 @@ def test_loop_fused_residual_layernorm_matches_separate_launches(orc, monkeypatc
                                                                  gated):
     """At M > 1 the residual projections write K-part partials and one launch
     sums them, adds into h and computes the next LayerNorm.  It must give the
-    same bits as the split-K reduction (or the GEMM's own epilogue) followed
-    by the LayerNorm kernel (QG_FUSE_REDUCE_LN=0): h and every scratch region,
-    over several iterations (skinny with and without K parts, ring tiles with
+    same bits as the split-K reduction of the same partials followed by the
+    LayerNorm kernel (QG_FUSE_REDUCE_LN=0): h and every scratch region, over
+    several iterations (skinny with one and several K parts, ring tiles with
     and without a K split, INT4 and INT2, plain and gated)."""
     inp, blk, _ = _blocks(orc, M, bits, D, F, seed=M + D + F + bits, gated=gated)
     scratch = qg.alloc_loop_scratch(blk, M)
