@@ -571,9 +571,16 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
                 d[p] = (as_f16x2(biased) + gc.nbz) * gc.s2;
             }
             const f16x8 b = f16x8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+            // The slice's MFMAs at raised wave priority: where two waves share
+            // a SIMD (64- and 32-row tiles, two workgroups per CU) the issuer
+            // of MFMAs goes first and the other's dequantisation and LDS
+            // reads fill in behind (measured 2.5-10 % faster on the block's
+            // prefill shapes, bit-identical).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
                 acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[tm], b, acc[tm], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
             if (j < 7) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) a_cur[tm] = a_nxt[tm];
