@@ -191,7 +191,8 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     const int D = blk->D, F = blk->F;
     hipError_t e = hipSuccess;
     // At M == 1 the QKV GEMV computes the LayerNorm of h in its prologue;
-    // otherwise a LayerNorm kernel writes norm first.
+    // at M > 1 a LayerNorm kernel writes norm before the first iteration and
+    // the previous iteration's down-projection launch before the others.
     const bool gate = gated(blk);
     qg_half* g = gate ? (qg_half*)(base + L.g) : nullptr;
     const bool fuse_qkv = qg::gemm_fuses_layernorm(blk->qkv.bits, M, D, 3 * D);
@@ -235,8 +236,9 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
                                  L.ws_bytes},
                                 s);
         // FFN input: the first FFN projection (gate, else up) normalises h
-        // itself at M == 1 and stores norm; otherwise a LayerNorm kernel
-        // writes norm first.  With a gate, up multiplies silu(g) in.
+        // itself at M == 1 and stores norm; at M > 1 the out projection's
+        // launch wrote it (a LayerNorm kernel where D has no fused form).
+        // With a gate, up multiplies silu(g) in.
         const qg_weight* first = gate ? &blk->gate : &blk->up;
         qg::GemmArgs fa{norm, D, first, gate ? g : u, F, M, qg::kStore, nullptr, 0, ws,
                         L.ws_bytes};
