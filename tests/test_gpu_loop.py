@@ -131,8 +131,9 @@ def test_loop_measured_workloads_sampled_rows(orc, name, bits, M, L, rows):
 @pytest.mark.parametrize("M", [1, 16, 40])
 def test_loop_graph_replays_match_direct_enqueue(orc, M, monkeypatch):
     """The cached-graph path and the kernel-by-kernel path give the same bits;
-    every replay is checked, with eager library work and syncs in between."""
-    D, F = 256, 512
+    every replay is checked, with eager library work and syncs in between
+    (D = 1024 at M > 1 takes the fused end-and-LayerNorm launches)."""
+    D, F = (256, 512) if M == 1 else (1024, 1536)
     inp, blk, _ = _blocks(orc, M, 4, D, F, seed=21)
     h0 = inp.X.float().cuda()
     scratch = qg.alloc_loop_scratch(blk, M)
@@ -153,10 +154,11 @@ def test_loop_graph_replays_match_direct_enqueue(orc, M, monkeypatch):
         torch.cuda.synchronize()
 
 
-def test_loop_inside_caller_graph_capture(orc):
+@pytest.mark.parametrize("M,D,F", [(1, 256, 512), (16, 1024, 2048), (64, 1024, 1024)])
+def test_loop_inside_caller_graph_capture(orc, M, D, F):
     """Under a caller's stream capture the kernels are recorded into the
-    caller's graph; each replay must equal the eager result."""
-    D, F, M = 256, 512, 1
+    caller's graph; each replay must equal the eager result (D = 1024 at
+    M > 1: the residual projections' fused end-and-LayerNorm launches)."""
     inp, blk, _ = _blocks(orc, M, 4, D, F, seed=22)
     h0 = inp.X.float().cuda()
     scratch = qg.alloc_loop_scratch(blk, M)
