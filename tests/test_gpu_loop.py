@@ -82,9 +82,12 @@ def test_loop_skinny_k_parts(orc, bits, M):
     assert torch.equal(split, h)
 
 
-@pytest.mark.parametrize("M", [1, 16, 40])
-def test_loop_empty_range_split_and_repeat(orc, M):
-    D, F = 256, 512
+@pytest.mark.parametrize("M,D", [(1, 256), (16, 256), (40, 256), (16, 1024), (40, 2048)])
+def test_loop_empty_range_split_and_repeat(orc, M, D):
+    """(D = 1024 and 2048 at M > 1: a call's first LayerNorm is a kernel of
+    its own, the others come from the fused residual launches; the split
+    must still give the same bits.)"""
+    F = 512
     inp, blk, _ = _blocks(orc, M, 4, D, F, seed=11)
     h0 = inp.X.float().cuda()
     h = h0.clone()
