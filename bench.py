@@ -133,6 +133,34 @@ def pmc_target(qg, torch, workloads, launches: int = 50):
         f"{launches} copies of {COPY_BYTES} bytes")
 
 
+def pmc_prefill(qg, torch, workloads, launches: int = 10):
+    """Counter target for the MFMA kernels: the M=2048 down projection
+    (K=8192 -> N=2048, 128-row ring tiles) and the M=512 FFN up projection
+    (K=2048 -> N=8192, 64-row ring tiles), each launched `launches` times
+    after a warm-up, then a dense FP16 GEMM of the vendor library (4096^3,
+    torch.matmul) whose FLOP rate is known, to calibrate the MFMA-busy
+    counter."""
+    dev = "cuda"
+    for (M, K, N) in ((2048, 8192, 2048), (512, 2048, 8192)):
+        W, X = workloads.single_gemm(M, K, N, seed=0)
+        p = qg.qg_pack(W.to(dev), 4)
+        Xd = X.to(dev)
+        Y = torch.empty(M, N, dtype=torch.float16, device=dev)
+        for _ in range(3):
+            qg.qg_gemm_int4(Xd, p, Y=Y)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            qg.qg_gemm_int4(Xd, p, Y=Y)
+        torch.cuda.synchronize()
+    a = torch.randn(4096, 4096, device=dev, dtype=torch.float16)
+    b = torch.randn(4096, 4096, device=dev, dtype=torch.float16)
+    c = torch.empty(4096, 4096, device=dev, dtype=torch.float16)
+    for _ in range(3 + launches):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    log(f"pmc prefill: {launches} launches each of the two ring GEMMs and the dense 4096^3 GEMM")
+
+
 def traffic_from(fetch_csv: str, write_csv: str, command: str):
     """HBM bytes per launch of the roofline GEMV from two rocprofv3 --pmc runs
     of --pmc-target (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
@@ -406,6 +434,9 @@ def main():
     ap.add_argument("--pmc-target", action="store_true",
                     help="only launch the roofline kernel and the calibration copy (for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="only launch the two ring GEMMs and a dense FP16 GEMM (for rocprofv3 "
+                         "--pmc SQ counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter runs (no GPU)")
     ap.add_argument("--traffic-command", default="",
@@ -431,6 +462,9 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_target:
         pmc_target(qg, torch, workloads)
+        return
+    if args.pmc_prefill:
+        pmc_prefill(qg, torch, workloads)
         return
 
     # ---- main leg: INT4 loop block, M=1, L=8 (decode)
