@@ -8,7 +8,10 @@ numpy) and imports nothing from the product package.
 Each function follows a passage of the TinyLoop documentation pages; see the
 header of oracle.c for the passages and for the readings taken where the pages
 are silent.  `brute.py` beside this file re-derives pack and GEMM with exact
-rational arithmetic for tiny shapes.
+rational arithmetic for tiny shapes.  Parity unpinned against the pages: the
+loop's glue readings (LayerNorm, self-only attention, identity FFN activation)
+and the integer zero-point convention, pinned only to closed forms of those
+readings.
 """
 from __future__ import annotations
 

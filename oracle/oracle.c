@@ -39,6 +39,11 @@
  *    weight, see or_block); FP16 rounding at the LN outputs and at
  *    every GEMM output, FP64 residual.
  *
+ * Parity unpinned against the pages: the glue readings above (LayerNorm,
+ * self-only attention, identity FFN activation) and the integer zero-point
+ * convention.  The pages print no values for them; the tests pin them only to
+ * closed forms of these readings.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <math.h>
