@@ -155,7 +155,13 @@ size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M);
  * the call it holds the last iteration's FP16 intermediates at the offsets
  * given by qg_loop_scratch_offsets (norm = second LN output [M][D],
  * qkv [M][3D], u [M][F] = the down projection's input, y = last
- * down-projection output [M][D], and with a gate g = gate output [M][F]). */
+ * down-projection output [M][D], and with a gate g = gate output [M][F]).
+ * Outside stream capture the iterations replay from a library-cached graph
+ * (keyed by every pointer and size above; see qg_release_cache).  Inside a
+ * caller's capture on `stream` the kernels are enqueued one by one, so the
+ * call can be part of the caller's graph; qg_gemm_int4 / qg_gemm_int2 only
+ * enqueue kernels and may be captured too, while qg_pack and
+ * qg_requant_4to2 synchronise and may not. */
 int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
                   void* scratch, size_t scratch_bytes, void* stream);
 size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M);
