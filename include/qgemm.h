@@ -161,7 +161,8 @@ size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M);
  * caller's capture on `stream` the kernels are enqueued one by one, so the
  * call can be part of the caller's graph; qg_gemm_int4 / qg_gemm_int2 only
  * enqueue kernels and may be captured too, while qg_pack and
- * qg_requant_4to2 synchronise and may not. */
+ * qg_requant_4to2 synchronise: on a stream under capture they return
+ * QG_EINVAL before enqueuing anything. */
 int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
                   void* scratch, size_t scratch_bytes, void* stream);
 size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M);

@@ -381,11 +381,19 @@ StatusWord g_pack_status[64];
 
 // Enqueues launch(status, tag) on s with the current device's status word
 // and a fresh tag, copies the word back and synchronises s; *bad is set when
-// the launch reported a failure.  Caller holds g_pack_mu.
+// the launch reported a failure.  Caller holds g_pack_mu.  Refused, before
+// anything is enqueued or allocated, on a stream that is being captured: the
+// read-back and the synchronisation cannot be part of a graph.
 template <class Launch>
 int run_with_status(const char* fn, hipStream_t s, Launch&& launch, int* bad) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(QG_EINVAL, "%s: the stream is being captured; this call synchronises its "
+                               "stream and cannot be part of a graph", fn);
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(fn, e);
     if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
     StatusWord& w = g_pack_status[dev];

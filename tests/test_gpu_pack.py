@@ -93,6 +93,37 @@ def test_status_word_reports_each_call_alone(orc):
     _assert_pack_equal(qg.qg_pack(good.cuda(), 2), orc.pack(good.numpy(), 2))
 
 
+def test_pack_and_requant_refused_under_capture(orc):
+    """qg_pack and qg_requant_4to2 synchronise their stream, so on a stream
+    under graph capture they are refused before anything is enqueued: the
+    capture stays valid (a GEMM captured beside them replays to the eager
+    result) and both calls work again once the capture has ended."""
+    W, X = workloads.single_gemm(4, 256, 64, seed=6)
+    Wd, Xd = W.cuda(), X.cuda()
+    p = qg.qg_pack(Wd, 4)
+    ref = f16_bits(qg.qg_gemm_int4(Xd, p))
+    Y = torch.empty(4, 64, dtype=torch.float16, device="cuda")
+    out4 = qg.PackedWeight.empty(256, 64, 4, Wd.device)
+    out2 = qg.PackedWeight.empty(256, 64, 2, Wd.device)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with pytest.raises(qg.QGValueError, match="captured"):
+            qg.qg_pack(Wd, 4, out=out4)
+        with pytest.raises(qg.QGValueError, match="captured"):
+            qg.qg_requant_4to2(p, out=out2)
+        qg.qg_gemm_int4(Xd, p, Y=Y)
+    for r in range(2):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(f16_bits(Y), ref), f"replay {r}"
+    op = orc.pack(W.numpy(), 4)
+    _assert_pack_equal(qg.qg_pack(Wd, 4, out=out4), op)
+    qg.qg_requant_4to2(p, out=out2)
+    _assert_pack_equal(out2, orc.requant_4to2(op))
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_unpack_and_dequant_bit_exact(orc, bits):
     W, _ = workloads.single_gemm(1, 1024, 96, seed=bits)
