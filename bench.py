@@ -450,7 +450,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU: this library has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 

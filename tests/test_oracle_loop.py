@@ -1,7 +1,7 @@
 """Pins for the oracle's LayerNorm stand-in and loop driver.
 
-The loop's glue (LayerNorm, self-only attention, identity FFN activation) is a
-reading of this build, not a passage of the pages; these tests pin the oracle
+The loop's glue (LayerNorm, self-only attention, identity FFN activation) is
+this library's reading, not a passage of the pages; these tests pin the oracle
 to that written reading with closed forms: LayerNorm of constructed rows,
 zero weights (residual unchanged), and diagonal weights, for which each
 iteration reduces to h += a*b*LN(h) followed by h += 2*c*d*LN(h).
