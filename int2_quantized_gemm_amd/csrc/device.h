@@ -46,6 +46,21 @@ struct Fmt {
     static constexpr int kQMax = (1 << BITS) - 1;
 };
 
+// 32-bit constants in registers the compiler cannot fold (an SGPR and a
+// VGPR), so that a mask and an OR constant meet in one fused VOP3 instruction
+// (v_and_or / v_bitop3), which can take neither a literal nor two SGPRs;
+// left as literals, each mask-and-or costs a v_and and a v_or.
+__device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ f16 as_f16(uint16_t v) { return __builtin_bit_cast(f16, v); }
@@ -165,6 +180,30 @@ __device__ __forceinline__ void epi_store(const OutEpi& e, int64_t m, int64_t n,
     if (e.kind == kGateMul) y = swiglu_f16(e.g[m * e.ldg + n], y);
     e.Y[m * e.ldy + n] = y;
     if (e.kind == kResidual) e.h[m * e.ldh + n] += (float)as_f16(y);
+}
+
+// The epilogue's input element (h[m][n] as FP32 bits for kResidual, g[m][n]
+// for kGateMul, 0 for kStore), for kernels that load it ahead of their
+// arithmetic; epi_store_pre then finishes exactly like epi_store.  The load is
+// one unconditional aligned dword (a control-flow split would make the
+// compiler wait for every load in flight at the join): h[m][n] itself, or the
+// dword of g holding g[m][n] (g 4-byte aligned, ldg even), or for kStore any
+// valid dword (`any`).
+__device__ __forceinline__ uint32_t epi_input(const OutEpi& e, int64_t m, int64_t n,
+                                              const uint32_t* any) {
+    const bool res = e.kind == kResidual, gm = e.kind == kGateMul;
+    const uint32_t* p = res ? (const uint32_t*)(e.h + m * e.ldh + n)
+                            : gm ? (const uint32_t*)(e.g + m * e.ldg + (n & ~int64_t(1))) : any;
+    const uint32_t v = *p;
+    return gm ? (v >> (16 * (int)(n & 1))) & 0xFFFFu : v;
+}
+
+__device__ __forceinline__ void epi_store_pre(const OutEpi& e, int64_t m, int64_t n, float acc,
+                                              uint32_t in) {
+    uint16_t y = f32_to_f16_bits(acc);
+    if (e.kind == kGateMul) y = swiglu_f16((uint16_t)in, y);
+    e.Y[m * e.ldy + n] = y;
+    if (e.kind == kResidual) e.h[m * e.ldh + n] = __builtin_bit_cast(float, in) + (float)as_f16(y);
 }
 
 }  // namespace qg

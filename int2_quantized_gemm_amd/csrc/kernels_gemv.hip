@@ -46,8 +46,20 @@ struct GemvMath {
     // Pair index (relative to the chunk) of class j, half h (h = 1: word >> 8).
     static __device__ __forceinline__ int pair(int q, int h, int j) { return q * PPW + j + NC * h; }
 
+    // The class masks (in SGPRs) and the bias (in a VGPR), so that each
+    // mask-and-or is one instruction.
+    struct Consts {
+        uint32_t mask[NC];
+        uint32_t bias;
+        __device__ __forceinline__ Consts() {
+#pragma unroll
+            for (int j = 0; j < NC; ++j) mask[j] = sgpr_const(F::kPairMask << (BITS * j));
+            bias = vgpr_const(kBias2);
+        }
+    };
+
     static __device__ __forceinline__ void accumulate(const Chunk& w, const f16x2* xp,
-                                                      float acc[NC]) {
+                                                      const Consts& k, float acc[NC]) {
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
             const uint32_t v[2] = {w[q], w[q] >> 8};
@@ -55,9 +67,8 @@ struct GemvMath {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int j = 0; j < NC; ++j)
-                    acc[j] = __builtin_amdgcn_fdot2(
-                        as_f16x2((v[h] & (F::kPairMask << (BITS * j))) | kBias2),
-                        xp[pair(q, h, j)], acc[j], false);
+                    acc[j] = __builtin_amdgcn_fdot2(as_f16x2((v[h] & k.mask[j]) | k.bias),
+                                                    xp[pair(q, h, j)], acc[j], false);
         }
     }
 
@@ -128,57 +139,85 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     const bool active = row0 < N;
     if (!LN && !active) return;  // (LN variants keep every wave for the barriers)
 
-    // Issue the weight loads of this wave first; the activations and their
-    // LayerNorm are computed while they are in flight.
+    // Load order.  Vector-memory loads of a wave complete in issue order, so
+    // the activations (or the LayerNorm input) go first: the arithmetic that
+    // needs only them (the LayerNorm, the per-chunk activation sums) then
+    // waits for them alone and runs while the weight loads are in flight, and
+    // each chunk's dot products wait only for that chunk's codes.  Every load
+    // is unconditional (rows past N read row N - 1 and are never stored), so
+    // no branch splits the loads into dependent round trips.
+    constexpr int VPT = LN ? K / 256 : 4;  // LayerNorm values per thread
+    float4 hv[VPT / 4];
+    u32x4 xv[CPR][PAIRS / 4];
+    if constexpr (LN) {
+        static_assert(K % 1024 == 0, "K must be a multiple of 1024 for the fused LayerNorm");
+        const float4* hp = (const float4*)(hln + threadIdx.x * VPT);
+#pragma unroll
+        for (int i = 0; i < VPT / 4; ++i) hv[i] = hp[i];
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const u32x4* xp = (const u32x4*)(X + (c * LPR + sub) * 32);
+#pragma unroll
+            for (int v = 0; v < PAIRS / 4; ++v) xv[c][v] = xp[v];
+        }
+    }
+
     typename G::Chunk wv[NW][U][CPR];
     uint16_t sv[NW][U][CPR], zv[NW][U][CPR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int row = row0 + u * RPW + rsub;
+        const int row = min(row0 + u * RPW + rsub, N - 1);
 #pragma unroll
         for (int b = 0; b < NW; ++b)
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
                 const int wi = (c * LPR + sub) * WPL;
-                if (row < N) {
-                    wv[b][u][c] =
-                        *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * wpr + wi);
-                    const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
-                    sv[b][u][c] = W.scales[b][sg];
-                    zv[b][u][c] = W.zeros[b][sg];
-                } else {
-                    wv[b][u][c] = typename G::Chunk{};
-                    sv[b][u][c] = 0;
-                    zv[b][u][c] = 0;
-                }
+                wv[b][u][c] = *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * wpr + wi);
+                const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
+                sv[b][u][c] = W.scales[b][sg];
+                zv[b][u][c] = W.zeros[b][sg];
             }
     }
+    // The epilogue's own input (the residual element, or the gate output),
+    // loaded with the rest so that the store does not wait for a round trip.
+    uint32_t ein[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int row = min(row0 + u * RPW + rsub, N - 1);
+        ein[u] = NW == 1 ? epi_input(out, 0, row, W.codes[0]) : 0u;
+    }
+    // Keep the compiler's scheduler from sinking loads into the arithmetic
+    // below (it would, to save registers, and each sunk load then costs a
+    // memory round trip of its own).
+    __builtin_amdgcn_sched_barrier(0);
 
     // Activations for this lane's k positions, reused for every row.
     f16x2 xr[CPR][PAIRS];
     if constexpr (LN) {
-        constexpr int VPT = K / 256;  // values per thread
-        static_assert(VPT % 4 == 0, "K must be a multiple of 1024 for the fused LayerNorm");
+        // The workgroup's 256 threads normalise the row once: mean, then the
+        // population variance of the centred values (eps 1e-5), each reduced
+        // by DPP in every wave and then in wave order through LDS; the FP16
+        // result is staged in LDS for the lanes to pick up.  The barriers
+        // wait for LDS traffic only, never for the weight loads in flight.
         __shared__ uint32_t xl[K / 2];
         __shared__ float part[2][4];
         const int t = threadIdx.x;
         const int w = t >> 6;
         float v[VPT];
-        const float4* hp = (const float4*)(hln + t * VPT);
 #pragma unroll
         for (int i = 0; i < VPT / 4; ++i) {
-            const float4 q = hp[i];
-            v[4 * i] = q.x;
-            v[4 * i + 1] = q.y;
-            v[4 * i + 2] = q.z;
-            v[4 * i + 3] = q.w;
+            v[4 * i] = hv[i].x;
+            v[4 * i + 1] = hv[i].y;
+            v[4 * i + 2] = hv[i].z;
+            v[4 * i + 3] = hv[i].w;
         }
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) sum += v[i];
         sum = segment_sum<64>(sum);
         if (lane == 0) part[0][w] = sum;
-        __syncthreads();
+        lds_barrier();
         const float mean = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) / (float)K;
         float sq = 0.0f;
 #pragma unroll
@@ -188,7 +227,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         }
         sq = segment_sum<64>(sq);
         if (lane == 0) part[1][w] = sq;
-        __syncthreads();
+        lds_barrier();
         const float var = ((part[1][0] + part[1][1]) + (part[1][2] + part[1][3])) / (float)K;
         const float rstd = 1.0f / sqrtf(var + 1e-5f);
 #pragma unroll
@@ -200,7 +239,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
 #pragma unroll
             for (int i = 0; i < VPT / 2; ++i) op[i] = xl[t * (VPT / 2) + i];
         }
-        __syncthreads();
+        lds_barrier();
         if (!active) return;
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
@@ -210,18 +249,14 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         }
     } else {
 #pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const int k0 = (c * LPR + sub) * 32;
-            const u32x4* xp = (const u32x4*)(X + k0);
+        for (int c = 0; c < CPR; ++c)
 #pragma unroll
             for (int v = 0; v < PAIRS / 4; ++v) {
-                const u32x4 t = xp[v];
-                xr[c][4 * v + 0] = as_f16x2(t.x);
-                xr[c][4 * v + 1] = as_f16x2(t.y);
-                xr[c][4 * v + 2] = as_f16x2(t.z);
-                xr[c][4 * v + 3] = as_f16x2(t.w);
+                xr[c][4 * v + 0] = as_f16x2(xv[c][v].x);
+                xr[c][4 * v + 1] = as_f16x2(xv[c][v].y);
+                xr[c][4 * v + 2] = as_f16x2(xv[c][v].z);
+                xr[c][4 * v + 3] = as_f16x2(xv[c][v].w);
             }
-        }
     }
     float xs[CPR][G::NC], xs_all[CPR];
 #pragma unroll
@@ -232,6 +267,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         for (int j = 0; j < G::NC; ++j) xs_all[c] += xs[c][j];
     }
 
+    const typename G::Consts kc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc[NW];
@@ -243,7 +279,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                 float a[G::NC];
 #pragma unroll
                 for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
-                G::accumulate(wv[b][u][c], xr[c], a);
+                G::accumulate(wv[b][u][c], xr[c], kc, a);
                 const float t = G::centred(a, xs[c], xs_all[c], (float)as_f16(zv[b][u][c]));
                 acc[b] += t * (float)as_f16(sv[b][u][c]);
             }
@@ -252,7 +288,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         const int row = row0 + u * RPW + rsub;
         if (sub == 0 && row < N) {
             if constexpr (NW == 1) {
-                epi_store(out, 0, row, acc[0]);
+                epi_store_pre(out, 0, row, acc[0], ein[u]);
             } else {
                 const uint16_t g16 = f32_to_f16_bits(acc[0]);
                 gout[row] = g16;

@@ -285,20 +285,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     }
 }
 
-// 32-bit constants in registers the compiler cannot fold (an SGPR and a
-// VGPR), so that a mask and an OR constant meet in one fused VOP3 instruction
-// (v_and_or / v_bitop3), which can take neither a literal nor two SGPRs.
-__device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
-    uint32_t r;
-    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
-    return r;
-}
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-    uint32_t r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-    return r;
-}
-
 // ---- Deep-prefetch variant ("ring").  Every operand of a step reaches LDS by
 // LDS DMA (buffer_load_dwordx4 ... lds), issued ahead into rings of stages,
 // so global latency is hidden without holding data in registers and without
