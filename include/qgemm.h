@@ -142,6 +142,22 @@ int qg_gemm_int2(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, 
                  int32_t M, void* ws, size_t ws_bytes, void* stream);
 size_t qg_gemm_ws_bytes(const qg_weight* w, int32_t M);
 
+/* The GEMM of qg_gemm_int4 / qg_gemm_int2 (dispatching on w->bits, which
+ * must be 4 or 2) for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Instead of a caller's workspace it uses a library-owned static device
+ * workspace of 16 MiB (each GPU the library runs on holds its own copy until
+ * the process ends); it calls no allocator.  Same arguments, validation,
+ * kernels and results (bit for bit) as qg_gemm_int4 / qg_gemm_int2 with a
+ * workspace.  A shape whose qg_gemm_ws_bytes(w, M) exceeds 16 MiB is
+ * rejected with QG_EINVAL before anything is enqueued.  The workspace holds
+ * K-split partials only, every one written before it is read, so no call
+ * depends on what an earlier call left there; but every call on one GPU
+ * shares that GPU's copy, so two calls whose execution may overlap on one GPU
+ * (different streams without ordering between them) race. */
+int qg_gemm_static_ws(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y,
+                      int64_t ldy, int32_t M, void* stream);
+
 /* Iterations [L0, L1) of the shared block, in place on the FP32 residual
  * h [M][D] (run_loop_iters_range, "Warm-start mid-loop" page, internal flow:
  * the same weights are applied on every iteration).  Per iteration:

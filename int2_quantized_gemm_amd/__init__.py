@@ -59,6 +59,7 @@ def _load():
         "qg_gemm_int4": (C.c_int, [vp, i64, W, vp, i64, i32, vp, sz, vp]),
         "qg_gemm_int2": (C.c_int, [vp, i64, W, vp, i64, i32, vp, sz, vp]),
         "qg_gemm_ws_bytes": (sz, [W, i32]),
+        "qg_gemm_static_ws": (C.c_int, [vp, i64, W, vp, i64, i32, vp]),
         "qg_loop_range": (C.c_int, [B, vp, i32, i32, i32, vp, sz, vp]),
         "qg_loop_scratch_bytes": (sz, [B, i32]),
         "qg_loop_scratch_offsets": (C.c_int, [B, i32, C.POINTER(sz), C.POINTER(sz),
@@ -203,6 +204,26 @@ def qg_gemm_int2(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None
                  stream=None) -> torch.Tensor:
     """Y[M][N] = X[M][K] . dequant(w) for 2-bit w, FP16 in/out, FP32 accumulation."""
     return _gemm(lib.qg_gemm_int2, "qg_gemm_int2", X, w, Y, ws, stream)
+
+
+def qg_gemm_static_ws(X: torch.Tensor, w: PackedWeight, Y: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """qg_gemm_int4 / qg_gemm_int2 (by w.bits) on the library's static device
+    workspace: allocates nothing when Y is given."""
+    if X.dim() != 2 or X.shape[1] != w.K:
+        raise ValueError(f"X must be [M][{w.K}], got {tuple(X.shape)}")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if Y.dim() != 2 or tuple(Y.shape) != (M, w.N):
+        raise ValueError(f"Y must be [{M}][{w.N}], got {tuple(Y.shape)}")
+    if X.dtype != torch.float16 or Y.dtype != torch.float16 or X.stride(1) != 1 or Y.stride(1) != 1:
+        raise ValueError("X and Y must be row-major FP16 tensors")
+    cw = w.cstruct()
+    _check("qg_gemm_static_ws", lib.qg_gemm_static_ws(_dev(X, "X"), X.stride(0), C.byref(cw),
+                                                      _dev(Y, "Y"), Y.stride(0), M,
+                                                      _stream(stream)))
+    return Y
 
 
 @dataclass

@@ -73,8 +73,9 @@ int check_weight(const qg_weight* w, const char* fn, const char* name) {
     return QG_OK;
 }
 
-int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half* Y, int64_t ldy,
-               int32_t M, const void* ws, size_t ws_bytes, int bits, const char* fn) {
+// Everything but the workspace.
+int check_gemm_io(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half* Y,
+                  int64_t ldy, int32_t M, int bits, const char* fn) {
     int st = check_weight(w, fn, "w");
     if (st) return st;
     if (w->bits != bits)
@@ -91,6 +92,13 @@ int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half*
                     (long long)ldy, w->N);
     if (!aligned(X, 16) || !aligned(Y, 16))
         return fail(QG_EINVAL, "%s: X and Y must be 16-byte aligned", fn);
+    return QG_OK;
+}
+
+int check_gemm(const qg_half* X, int64_t ldx, const qg_weight* w, const qg_half* Y, int64_t ldy,
+               int32_t M, const void* ws, size_t ws_bytes, int bits, const char* fn) {
+    const int st = check_gemm_io(X, ldx, w, Y, ldy, M, bits, fn);
+    if (st || M == 0) return st;
     const size_t need = qg::gemm_ws_bytes(w->bits, M, w->K, w->N);
     if (ws_bytes < need)
         return fail(QG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
@@ -426,6 +434,37 @@ int run_with_status(const char* fn, hipStream_t s, Launch&& launch, int* bad) {
     return QG_OK;
 }
 
+// ---- static workspace of qg_gemm_static_ws (callers that cannot allocate).
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from module load until the process ends.  In host code `static_ws` is only
+// a host-side stand-in for the symbol; the device address of each GPU's copy
+// comes from hipGetSymbolAddress with that GPU current, once, and only that
+// address is ever handed to kernels.
+constexpr size_t kStaticWsBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t static_ws[kStaticWsBytes];
+
+std::mutex g_static_ws_mu;
+void* g_static_ws_ptr[64] = {nullptr};
+
+// Device address of the current device's static workspace (looked up on the
+// first call on that device); QG_OK or a failure status with its message.
+int static_ws_address(const char* fn, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= 64) return fail(QG_EHIP, "%s: device index %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_static_ws_mu);
+    if (!g_static_ws_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(static_ws));
+        if (e != hipSuccess || p == nullptr)
+            return hip_fail(fn, e != hipSuccess ? e : hipErrorInvalidSymbol);
+        g_static_ws_ptr[dev] = p;
+    }
+    *out = g_static_ws_ptr[dev];
+    return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -550,6 +589,29 @@ int qg_gemm_int4(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, 
 int qg_gemm_int2(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y, int64_t ldy,
                  int32_t M, void* ws, size_t ws_bytes, void* stream) {
     return gemm_entry(X, ldx, w, Y, ldy, M, ws, ws_bytes, stream, 2, "qg_gemm_int2");
+}
+
+int qg_gemm_static_ws(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* Y,
+                      int64_t ldy, int32_t M, void* stream) {
+    const char* fn = "qg_gemm_static_ws";
+    int st = check_weight(w, fn, "w");
+    if (st) return st;
+    // validate as qg_gemm_int4 / qg_gemm_int2 (dispatching on w->bits), with
+    // the static workspace standing in for the caller's
+    const size_t need = qg::gemm_ws_bytes(w->bits, M < 0 ? 0 : M, w->K, w->N);
+    if (need > kStaticWsBytes)
+        return fail(QG_EINVAL, "%s: this shape needs %zu bytes of workspace, more than the %zu "
+                               "of the static workspace (use qg_gemm_int%d with a workspace)",
+                    fn, need, kStaticWsBytes, w->bits);
+    st = check_gemm_io(X, ldx, w, Y, ldy, M, w->bits, fn);
+    if (st) return st;
+    if (M == 0) return ok();
+    void* ws = nullptr;
+    if (need > 0 && (st = static_ws_address(fn, &ws)) != QG_OK) return st;
+    qg::GemmArgs a{X, ldx, w, Y, ldy, M, qg::kStore, nullptr, 0, ws, need};
+    hipError_t e = qg::launch_gemm(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
 }
 
 size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M) {

@@ -250,3 +250,43 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True,
                        timeout=300)
     assert "IMPORT-ERROR" in r.stdout and "no fallback" in r.stdout, r.stdout + r.stderr
+
+
+def _gemm_static(w, X=FAKE, ldx=None, Y=FAKE, ldy=None, M=1):
+    ldx = w.K if ldx is None else ldx
+    ldy = w.N if ldy is None else ldy
+    return qg.lib.qg_gemm_static_ws(X, ldx, C.byref(w), Y, ldy, M, None)
+
+
+def test_static_ws_rejects_shapes_beyond_its_workspace():
+    """A shape whose K-split workspace exceeds the 16 MiB static workspace is
+    refused on the host, before anything is enqueued, and names the sizes;
+    the loop block's shapes up to M = 512 fit."""
+    w = _w(bits=4, K=8192, N=2048)
+    need = qg.lib.qg_gemm_ws_bytes(C.byref(w), 768)
+    assert need > 16 << 20
+    assert _gemm_static(w, M=768) == qg.QG_EINVAL
+    msg = qg.qg_last_error()
+    assert "static workspace" in msg and str(need) in msg
+    for K, N in ((2048, 6144), (2048, 2048), (2048, 8192), (8192, 2048)):
+        for M in range(1, 513):
+            assert qg.lib.qg_gemm_ws_bytes(C.byref(_w(bits=4, K=K, N=N)), M) <= 16 << 20
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(bits=3), qg.QG_EUNSUPPORTED, "bits"),
+    (dict(K=100), qg.QG_EINVAL, "K"),
+    (dict(codes=FAKE + 4), qg.QG_EINVAL, "aligned"),
+])
+def test_static_ws_rejects_bad_weight(kw, code, needle):
+    assert _gemm_static(_w(**kw)) == code
+    assert needle in qg.qg_last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ldx=2040), "ldx"), (dict(ldy=100), "ldy"), (dict(M=-1), "M"), (dict(X=0), "NULL"),
+    (dict(Y=FAKE + 2), "aligned"),
+])
+def test_static_ws_rejects_bad_operands(kw, needle):
+    assert _gemm_static(_w(), **kw) == qg.QG_EINVAL
+    assert needle in qg.qg_last_error()
