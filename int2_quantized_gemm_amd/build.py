@@ -19,6 +19,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["qgemm.hip", "kernels_pack.hip", "kernels_gemm.hip", "kernels_gemv.hip",
            "kernels_prefill.hip", "kernels_loop.hip", "kernels_requant.hip"]
 ARCH = os.environ.get("QG_OFFLOAD_ARCH", "gfx950")
+# read-only bandwidth probe used by bench.py for its memory ceilings
+BENCH_SOURCE = "membench.hip"
+BENCH_LIB = os.path.join(HERE, "libqgbench.so")
 
 CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
@@ -54,6 +57,17 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    # the benchmark's read-bandwidth probe, a library of its own
+    obj = _compile(BENCH_SOURCE)
+    tmp = BENCH_LIB + ".tmp"
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc link failed (bench probe)")
+    os.replace(tmp, BENCH_LIB)
+    if verbose:
+        print(f"built {BENCH_LIB}")
     return LIB
 
 
