@@ -31,9 +31,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     in stream order and the call returns without synchronising unless the
  *     entry says otherwise.  Kernel faults surface at the caller's next sync.
- *   - Every argument is validated on the host before anything is enqueued; on
- *     a non-zero return nothing was enqueued and no output was touched.
- *     qg_last_error() (thread-local) then names the failed check.
+ *   - Every argument is validated before any output is written; on a non-zero
+ *     return no output was touched (and, apart from the validation pass of
+ *     qg_pack / qg_requant_4to2, which writes nothing, nothing was
+ *     enqueued).  qg_last_error() (thread-local) then names the failed check.
  *   - Calls on the same outputs/scratch from two streams race; calls on
  *     distinct buffers may run concurrently.
  *   - Results are deterministic: the same call on the same inputs gives the
@@ -107,8 +108,12 @@ const char* qg_last_error(void);
  * group: 128, or K for per-row groups (QG_EUNSUPPORTED otherwise).
  * codes [N][K*bits/32], scales and zeros [N][K/group] are written in full.
  * Bit-identical to the definition (FP64 arithmetic on the device).
- * Synchronises `stream` before returning, because it reports non-finite W or
- * a scale that overflows FP16 as QG_EINVAL (outputs are then unspecified). */
+ * Runs in two passes on `stream`: a validation pass that computes every
+ * group's range and scale and writes nothing (no output at all), then, after
+ * synchronising `stream` to read its verdict, the packing pass.  Non-finite W
+ * or a scale that overflows FP16 returns QG_EINVAL with codes, scales and
+ * zeros untouched; otherwise the packing pass is enqueued and the call
+ * returns without waiting for it (stream order, like every other call). */
 int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int32_t group,
             uint32_t* codes, qg_half* scales, qg_half* zeros, void* stream);
 
@@ -123,10 +128,14 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
  * overlap w4's or each other.  In place: w2->codes == w4->codes writes the
  * INT2 codes compactly over the first half of the INT4 code buffer (the rest
  * is left as it was), and w2->scales == w4->scales / w2->zeros == w4->zeros
- * overwrite those arrays; any other overlap is QG_EINVAL.  Synchronises `stream` before returning (the caller may free
- * or reuse the INT4 buffers at once), because it reports a non-finite INT4
- * scale or zero, or an INT2 scale that overflows FP16, as QG_EINVAL (outputs
- * are then unspecified). */
+ * overwrite those arrays; any other overlap is QG_EINVAL.  Runs in two
+ * passes on `stream`, like qg_pack: a validation pass that writes nothing,
+ * then, after synchronising `stream` to read its verdict, the re-quantisation.
+ * A non-finite INT4 scale or zero, or an INT2 scale that overflows FP16,
+ * returns QG_EINVAL with w2 (and, in place, w4) untouched; otherwise the
+ * re-quantisation is enqueued and the call returns without waiting for it:
+ * free or reuse the INT4 buffers only after that work (stream order, as the
+ * pages' tier switch frees them after a stream sync). */
 int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream);
 
 /* Y[M][N] = X[M][K] . dequant(w)[K][N] (quant_gemm, "β-Informed Deployment

@@ -157,7 +157,9 @@ class PackedWeight:
 
 def qg_pack(W: torch.Tensor, bits: int, group: int = GROUP, out: PackedWeight | None = None,
             stream=None) -> PackedWeight:
-    """Quantise FP32 W [K][N] (GPU) into layout v1; synchronises the stream."""
+    """Quantise FP32 W [K][N] (GPU) into layout v1: a validation pass (which
+    synchronises the stream and raises, with nothing written, on non-finite W
+    or an overflowing scale), then the packing, enqueued on the stream."""
     if W.dtype != torch.float32 or W.dim() != 2 or W.stride(1) != 1:
         raise ValueError("W must be a row-major FP32 [K][N] tensor")
     K, N = W.shape
@@ -323,7 +325,10 @@ def qg_release_cache() -> None:
 
 def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place: bool = False,
                     stream=None) -> PackedWeight:
-    """INT4 -> INT2 re-quantisation on the GPU; synchronises the stream.
+    """INT4 -> INT2 re-quantisation on the GPU: a validation pass (which
+    synchronises the stream and raises, with nothing written, on a non-finite
+    INT4 scale or zero or an overflowing INT2 scale), then the re-quantisation,
+    enqueued on the stream.
 
     Out of place the result goes to `out` (or new tensors).  With
     in_place=True the INT2 codes are written compactly over the front of
@@ -349,9 +354,9 @@ def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place:
 def requant_block(blk: Block, in_place: bool = False, stream=None) -> Block:
     """The INT4 -> INT2 tier switch of a loop block ("β-Informed Deployment
     Features" page, CTX-TIER apply step): re-quantise each INT4 projection
-    (INT2 ones are kept).  Each call has synchronised the stream when it
-    returns, so the INT4 tensors may be dropped (out of place) as soon as the
-    caller releases `blk`."""
+    (INT2 ones are kept).  The re-quantisations are enqueued on the stream;
+    torch's allocator is stream-ordered, so the INT4 tensors may be dropped
+    (out of place) as soon as the caller releases `blk`."""
     ws = {k: qg_requant_4to2(w, in_place=in_place, stream=stream) if w.bits == 4 else w
           for k, w in blk.weights().items()}
     return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))

@@ -19,15 +19,19 @@ inline SzIdx sz_idx(const qg_weight& w) {
 inline bool per_row(const qg_weight& w) { return w.group != kGroup; }
 
 // ---- pack / unpack / dequant (kernels_pack.hip)
-// Pack and re-quantisation report a non-finite input or an FP16 scale
-// overflow by storing `tag` (the caller's nonzero call tag) into *status;
-// the word is never cleared, so the caller compares it with its own tag.
+// Pack and re-quantisation run in two passes.  The validation pass writes
+// nothing but, when the input holds a non-finite value or a scale overflows
+// FP16, `tag` (the caller's nonzero call tag) into *status; the word is never
+// cleared, so the caller compares it with its own tag.  The writing pass is
+// launched only after a clean validation pass.
+hipError_t launch_pack_check(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                             int* status, int tag, hipStream_t s);
 hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
-                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status, int tag,
-                       hipStream_t s);
+                       uint32_t* codes, qg_half* scales, qg_half* zeros, hipStream_t s);
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s);
+hipError_t launch_requant_4to2_check(const qg_weight& w4, int* status, int tag, hipStream_t s);
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
-                               int* status, int tag, hipStream_t s);
+                               hipStream_t s);
 // Largest K the per-row re-quantisation holds in one workgroup's registers.
 constexpr int kRequantRowMaxK = 32768;
 hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t s);

@@ -17,7 +17,11 @@ namespace qg {
 namespace {
 
 // PER_ROW: gl = K (runtime); otherwise gl = 128, a compile-time loop bound.
-template <int BITS, bool PER_ROW>
+// CHECK: the validation pass -- the same range and scale, then the call's tag
+// stored to *status when W holds a non-finite value or the scale overflows
+// FP16, and nothing else written; the packing pass (CHECK false) runs only
+// after a clean validation pass and writes codes, scales and zeros.
+template <int BITS, bool PER_ROW, bool CHECK>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64_t ldw, int K,
                                               int N, uint32_t* __restrict__ codes,
                                               uint16_t* __restrict__ scales,
@@ -42,6 +46,10 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64
     const uint16_t s_bits = f64_to_f16_bits((hi - lo) / (double)F::kQMax);
     double s = f16_bits_to_f64(s_bits);
     bad |= !isfinite(s);
+    if constexpr (CHECK) {
+        if (bad) *status = tag;  // every failing thread stores the same call tag
+        return;
+    }
     uint16_t s_store = s_bits;
     if (s == 0.0) {
         s = 1.0;
@@ -60,13 +68,12 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64
         for (int j = 0; j < F::kCodesPerWord; ++j) {
             const int k = wi * F::kCodesPerWord + j;
             double q = rint((double)col[(int64_t)k * ldw] / s) + z;
-            q = q >= 0.0 ? q : 0.0;  // also maps NaN to 0 (reported via status)
+            q = q >= 0.0 ? q : 0.0;
             q = q > (double)F::kQMax ? (double)F::kQMax : q;
             word |= (uint32_t)q << (16 * (j & 1) + BITS * (j >> 1));
         }
         out[wi] = word;
     }
-    if (bad) *status = tag;  // every failing thread stores the same call tag
 }
 
 // One thread per packed word: writes the word's codes q[n][k] as bytes.
@@ -120,20 +127,32 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
 
 }  // namespace
 
-hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
-                       uint32_t* codes, qg_half* scales, qg_half* zeros, int* status, int tag,
-                       hipStream_t s) {
+template <bool CHECK>
+hipError_t launch_pack_pass(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                            uint32_t* codes, qg_half* scales, qg_half* zeros, int* status,
+                            int tag, hipStream_t s) {
     dim3 grid((N + 255) / 256, K / group);
     const bool row = group != kGroup;
     if (bits == 4 && row)
-        k_pack<4, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
+        k_pack<4, true, CHECK><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else if (bits == 4)
-        k_pack<4, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
+        k_pack<4, false, CHECK><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else if (row)
-        k_pack<2, true><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
+        k_pack<2, true, CHECK><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     else
-        k_pack<2, false><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
+        k_pack<2, false, CHECK><<<grid, 256, 0, s>>>(W, ldw, K, N, codes, scales, zeros, status, tag);
     return hipGetLastError();
+}
+
+hipError_t launch_pack_check(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                             int* status, int tag, hipStream_t s) {
+    return launch_pack_pass<true>(W, ldw, K, N, bits, group, nullptr, nullptr, nullptr, status,
+                                  tag, s);
+}
+
+hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int group,
+                       uint32_t* codes, qg_half* scales, qg_half* zeros, hipStream_t s) {
+    return launch_pack_pass<false>(W, ldw, K, N, bits, group, codes, scales, zeros, nullptr, 0, s);
 }
 
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s) {

@@ -46,6 +46,11 @@
 namespace qg {
 namespace {
 
+// CHECK: the validation pass -- each group's INT4 scale and zero and new INT2
+// scale, then the call's tag stored to *status when one is non-finite (or
+// the INT2 scale overflows FP16), and nothing else written; the writing pass
+// (CHECK false) runs only after a clean validation pass.
+template <bool CHECK>
 __global__ __launch_bounds__(256) void k_requant_4to2(
     const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
     int g0, int gcount, uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status,
@@ -87,6 +92,10 @@ __global__ __launch_bounds__(256) void k_requant_4to2(
     uint16_t s_store = f64_to_f16_bits((hi - lo) / 3.0);
     double s2 = f16_bits_to_f64(s_store);
     const bool bad = live && (!isfinite(s4) || !isfinite(z4) || !isfinite(s2));
+    if constexpr (CHECK) {
+        if (bad) *status = tag;  // every failing thread stores the same call tag
+        return;
+    }
     if (s2 == 0.0) {
         s2 = 1.0;
         s_store = 0x3c00;  // 1.0
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(256) void k_requant_4to2(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         double q = rint((((double)(4 * r + v) - z4) * s4) / s2) + z2;
-        q = q >= 0.0 ? q : 0.0;  // also maps NaN to 0 (reported via status)
+        q = q >= 0.0 ? q : 0.0;
         q = q > 3.0 ? 3.0 : q;
         table |= (uint32_t)q << (2 * (4 * r + v));
     }
@@ -121,13 +130,13 @@ __global__ __launch_bounds__(256) void k_requant_4to2(
         scales2[sg] = s_store;
         zeros2[sg] = f64_to_f16_bits(z2);
     }
-    if (bad) *status = tag;  // every failing thread stores the same call tag
 }
 
 // Per-row groups: workgroup x covers row row0 + x; thread t takes
 // INT2 words t, t + 256, ... of the row (INT4 words 2j, 2j + 1 for INT2 word j).
 constexpr int kRowPairs = kRequantRowMaxK / 16 / 256;  // INT2 words per thread, at most
 
+template <bool CHECK>
 __global__ __launch_bounds__(256) void k_requant_4to2_row(
     const uint32_t* codes4, const uint16_t* scales4, const uint16_t* zeros4, int K, int row0,
     uint32_t* codes2, uint16_t* scales2, uint16_t* zeros2, int* status, int tag) {
@@ -172,6 +181,10 @@ __global__ __launch_bounds__(256) void k_requant_4to2_row(
     uint16_t s_store = f64_to_f16_bits((hi - lo) / 3.0);
     double s2 = f16_bits_to_f64(s_store);
     const bool bad = !isfinite(s4) || !isfinite(z4) || !isfinite(s2);
+    if constexpr (CHECK) {
+        if (t == 0 && bad) *status = tag;
+        return;
+    }
     if (s2 == 0.0) {
         s2 = 1.0;
         s_store = 0x3c00;  // 1.0
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256) void k_requant_4to2_row(
     z2 = z2 < 0.0 ? 0.0 : (z2 > 3.0 ? 3.0 : z2);
     if (t < 16) {
         double q = rint((((double)t - z4) * s4) / s2) + z2;
-        q = q >= 0.0 ? q : 0.0;  // also maps NaN to 0 (reported via status)
+        q = q >= 0.0 ? q : 0.0;
         q = q > 3.0 ? 3.0 : q;
         tab[t] = (uint32_t)q;
     }
@@ -206,14 +219,28 @@ __global__ __launch_bounds__(256) void k_requant_4to2_row(
     if (t == 0) {
         scales2[n] = s_store;
         zeros2[n] = f64_to_f16_bits(z2);
-        if (bad) *status = tag;  // every failing thread stores the same call tag
     }
 }
 
 }  // namespace
 
+hipError_t launch_requant_4to2_check(const qg_weight& w4, int* status, int tag, hipStream_t s) {
+    const int K = w4.K, N = w4.N, groups = K / kGroup;
+    if (per_row(w4)) {
+        k_requant_4to2_row<true><<<(unsigned)N, 256, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, 0,
+                                                             nullptr, nullptr, nullptr, status, tag);
+        return hipGetLastError();
+    }
+    const int lanes = groups * 4;
+    const int threads = lanes >= 256 ? 256 : (lanes + 63) / 64 * 64;
+    const dim3 grid((unsigned)((lanes + threads - 1) / threads), (unsigned)N);
+    k_requant_4to2<true><<<grid, threads, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, 0, 0, groups,
+                                                  nullptr, nullptr, nullptr, status, tag);
+    return hipGetLastError();
+}
+
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
-                               int* status, int tag, hipStream_t s) {
+                               hipStream_t s) {
     const int K = w4.K, N = w4.N, groups = K / kGroup;
     uint32_t* c2 = const_cast<uint32_t*>(w2.codes);
     uint16_t* s2 = const_cast<uint16_t*>(w2.scales);
@@ -223,14 +250,14 @@ hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in
         const int lanes = gcount * 4;
         const int threads = lanes >= 256 ? 256 : (lanes + 63) / 64 * 64;
         const dim3 grid((unsigned)((lanes + threads - 1) / threads), (unsigned)rows);
-        k_requant_4to2<<<grid, threads, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, row0, g0,
-                                                gcount, c2, s2, z2, status, tag);
+        k_requant_4to2<false><<<grid, threads, 0, s>>>(w4.codes, w4.scales, w4.zeros, K, row0, g0,
+                                                       gcount, c2, s2, z2, nullptr, 0);
         return hipGetLastError();
     };
     if (per_row(w4)) {
         auto rows = [&](int64_t row0, int64_t count) {
-            k_requant_4to2_row<<<(unsigned)count, 256, 0, s>>>(w4.codes, w4.scales, w4.zeros, K,
-                                                               (int)row0, c2, s2, z2, status, tag);
+            k_requant_4to2_row<false><<<(unsigned)count, 256, 0, s>>>(
+                w4.codes, w4.scales, w4.zeros, K, (int)row0, c2, s2, z2, nullptr, 0);
             return hipGetLastError();
         };
         if (!in_place) return rows(0, N);

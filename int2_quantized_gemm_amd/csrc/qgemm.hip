@@ -387,11 +387,13 @@ struct StatusWord {
 std::mutex g_pack_mu;
 StatusWord g_pack_status[64];
 
-// Enqueues launch(status, tag) on s with the current device's status word
-// and a fresh tag, copies the word back and synchronises s; *bad is set when
-// the launch reported a failure.  Caller holds g_pack_mu.  Refused, before
-// anything is enqueued or allocated, on a stream that is being captured: the
-// read-back and the synchronisation cannot be part of a graph.
+// Enqueues the validation pass check(status, tag) on s with the current
+// device's status word and a fresh tag, copies the word back and
+// synchronises s; *bad is set when the pass reported a failure (the pass
+// writes nothing else, so on failure no output has been touched).  Caller
+// holds g_pack_mu.  Refused, before anything is enqueued or allocated, on a
+// stream that is being captured: the read-back and the synchronisation cannot
+// be part of a graph.
 template <class Launch>
 int run_with_status(const char* fn, hipStream_t s, Launch&& launch, int* bad) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -494,12 +496,14 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
     std::lock_guard<std::mutex> lock(g_pack_mu);
     int bad = 0;
     const int st = run_with_status(fn, s, [&](int* status, int tag) {
-        return qg::launch_pack(W, ldw, K, N, bits, group, codes, scales, zeros, status, tag, s);
+        return qg::launch_pack_check(W, ldw, K, N, bits, group, status, tag, s);
     }, &bad);
     if (st) return st;
     if (bad)
         return fail(QG_EINVAL, "%s: W holds a non-finite value or a group whose scale overflows "
                                "FP16", fn);
+    const hipError_t e = qg::launch_pack(W, ldw, K, N, bits, group, codes, scales, zeros, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
 
@@ -555,12 +559,14 @@ int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
     std::lock_guard<std::mutex> lock(g_pack_mu);
     int bad = 0;
     const int rc = run_with_status(fn, s, [&](int* status, int tag) {
-        return qg::launch_requant_4to2(*w4, *w2, in_place, status, tag, s);
+        return qg::launch_requant_4to2_check(*w4, status, tag, s);
     }, &bad);
     if (rc) return rc;
     if (bad)
         return fail(QG_EINVAL, "%s: w4 holds a non-finite scale or zero, or a group whose INT2 "
                                "scale overflows FP16", fn);
+    const hipError_t e = qg::launch_requant_4to2(*w4, *w2, in_place, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
 

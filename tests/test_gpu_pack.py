@@ -145,3 +145,58 @@ def test_unpack_hand_built_words(orc):
                         np.zeros((1, 1), np.uint16))
         q = qg.qg_unpack(to_gpu(op, qg)).cpu().numpy()[0]
         assert list(q[:per]) == case["codes"]
+
+
+def _same_bits(a, b):
+    """Bit-for-bit equality (NaN patterns included) of two tensors."""
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.float16 else a,
+                       b.view(torch.int16) if b.dtype == torch.float16 else b)
+
+
+def _canary_weight(K, N, bits, group=128):
+    """A packed-weight buffer set whose every byte holds a canary pattern."""
+    p = qg.PackedWeight.empty(K, N, bits, "cuda", group)
+    p.codes.fill_(0x5A5A5A5A)
+    p.scales.view(torch.int16).fill_(0x7BAD)
+    p.zeros.view(torch.int16).fill_(0x7BAD)
+    return p, [t.clone() for t in (p.codes, p.scales, p.zeros)]
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 256)])
+@pytest.mark.parametrize("bad", [np.nan, -np.inf, 3e38])
+def test_rejected_pack_leaves_outputs_untouched(bits, group, bad):
+    """A rejected qg_pack writes nothing: the validation pass runs first and
+    the packing pass is never enqueued, so canary-filled codes, scales and
+    zeros come back unchanged (also the groups of the call that were fine)."""
+    W = np.random.default_rng(3).standard_normal((256, 40)).astype(np.float32) * 0.02
+    W[200, 17] = bad
+    p, before = _canary_weight(256, 40, bits, group)
+    with pytest.raises(qg.QGValueError):
+        qg.qg_pack(torch.from_numpy(W).cuda(), bits, group=group, out=p)
+    torch.cuda.synchronize()
+    for a, b in zip((p.codes, p.scales, p.zeros), before):
+        assert _same_bits(a, b)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_rejected_requant_leaves_outputs_untouched(in_place):
+    """A rejected qg_requant_4to2 writes nothing: out of place the canary
+    INT2 buffers, in place the INT4 weight itself, come back unchanged."""
+    W, _ = workloads.single_gemm(1, 512, 48, seed=9)
+    p4 = qg.qg_pack(W.cuda(), 4)
+    p4.scales.view(torch.int16)[30, 2] = 0x7E00  # NaN
+    torch.cuda.synchronize()
+    if in_place:
+        before = [t.clone() for t in (p4.codes, p4.scales, p4.zeros)]
+        with pytest.raises(qg.QGValueError, match="non-finite"):
+            qg.qg_requant_4to2(p4, in_place=True)
+        torch.cuda.synchronize()
+        for a, b in zip((p4.codes, p4.scales, p4.zeros), before):
+            assert _same_bits(a, b)
+    else:
+        p2, before = _canary_weight(512, 48, 2)
+        with pytest.raises(qg.QGValueError, match="non-finite"):
+            qg.qg_requant_4to2(p4, out=p2)
+        torch.cuda.synchronize()
+        for a, b in zip((p2.codes, p2.scales, p2.zeros), before):
+            assert _same_bits(a, b)
