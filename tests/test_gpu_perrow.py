@@ -68,10 +68,7 @@ def test_perrow_gemm_paths(orc, bits, M, K, N):
     torch.cuda.synchronize()
     g.check()
     Y = g.view.float().cpu().numpy()
-    blk = 32 if M <= 400 else 64
-    rows = list(range(M)) if M <= 64 else sorted(
-        {r for b in range(0, M, blk) for r in (b, min(b + blk - 1, M - 1))} | {M - 1})
-    assert_close(Y[rows], orc.gemm(X.numpy()[rows], op),
+    assert_close(Y, orc.gemm(X.numpy(), op),
                  f"per-row bits={bits} M={M} K={K} N={N}")
 
 

@@ -50,6 +50,5 @@ def test_random_shape(orc, M, K, N, bits, per_row, ldx_pad):
     torch.cuda.synchronize()
     g.check()
     Y = g.view.float().cpu().numpy()
-    rows = sorted({r for b in range(0, M, 32) for r in (b, min(b + 31, M - 1))})
-    assert_close(Y[rows], orc.gemm(X.numpy()[rows], op),
+    assert_close(Y, orc.gemm(X.numpy(), op),
                  f"M={M} K={K} N={N} bits={bits} per_row={per_row} ldx={K + ldx_pad}")

@@ -74,8 +74,7 @@ def test_int2_gemm_after_requant(orc, M):
     p2 = qg.qg_requant_4to2(qg.qg_pack(W.cuda(), 4), in_place=True)
     ref_w = orc.requant_4to2(orc.pack(W.numpy(), 4))
     Y = qg.qg_gemm_int2(X.cuda(), p2).float().cpu().numpy()
-    rows = [0, M - 1] if M > 2 else [0]
-    assert_close(Y[rows], orc.gemm(X.numpy()[rows], ref_w), f"int2 gemm after requant M={M}")
+    assert_close(Y, orc.gemm(X.numpy(), ref_w), f"int2 gemm after requant M={M}")
 
 
 @pytest.mark.parametrize("in_place", [False, True])

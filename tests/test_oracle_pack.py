@@ -153,13 +153,25 @@ def test_pack_rejects_non_finite_and_overflow(orc):
     assert orc.half_to_double(p.scales[1, 0]) == 65504.0
 
 
-def test_loop_block_code_bytes_match_the_pages():
+def test_loop_block_code_bytes_match_the_pages(orc):
+    """The oracle's pack of the five-weight loop block (seeded N(0, 0.02)
+    weights of the page's shapes) gives exactly the page's 32 MB of INT4 codes
+    and 16 MB after the INT2 re-pack, i.e. K/2-byte INT4 and K/4-byte INT2
+    rows, and its re-quantisation frees the page's 16 MB."""
+    import workloads
     gd = golden("loop_block_bytes.json")
-    for bits, key in ((4, "int4_code_bytes_five"), (2, "int2_code_bytes_five")):
-        # codes [N][K*bits/32] uint32 per weight
-        total = sum(N * (K * bits // 32) * 4 for K, N in gd["five_weights_KN"])
-        assert total == gd[key]
-    assert gd["int4_code_bytes_five"] - gd["int2_code_bytes_five"] == gd["freed_bytes"]
-    # INT4 rows K/2 bytes, compact INT2 rows K/4 bytes (CTX-TIER kernel details)
-    for K, _ in gd["five_weights_KN"]:
-        assert (K * 4 // 32) * 4 == K // 2 and (K * 2 // 32) * 4 == K // 4
+    g = workloads.generator(0)
+    totals = {4: 0, 2: 0}
+    requant = 0
+    for K, N in gd["five_weights_KN"]:
+        W = workloads.weight(K, N, g).numpy()
+        p4 = orc.pack(W, 4)
+        p2 = orc.pack(W, 2)
+        assert p4.codes.shape == (N, K // 8) and p4.codes.dtype == np.uint32   # K/2 bytes a row
+        assert p2.codes.shape == (N, K // 16) and p2.codes.dtype == np.uint32  # K/4 bytes a row
+        totals[4] += p4.codes.nbytes
+        totals[2] += p2.codes.nbytes
+        requant += orc.requant_4to2(p4).codes.nbytes
+    assert totals[4] == gd["int4_code_bytes_five"]
+    assert totals[2] == gd["int2_code_bytes_five"] == requant
+    assert totals[4] - requant == gd["freed_bytes"]
