@@ -191,6 +191,32 @@ int qg_gemm_static_ws(const qg_half* X, int64_t ldx, const qg_weight* w, qg_half
 int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
                   void* scratch, size_t scratch_bytes, void* stream);
 size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M);
+
+/* Chunked prefill ("Model" page, Chunked prefill; Parameters: prefill_chunk):
+ * the chunk-first driver.  Rows [0, M) of h are split into chunks of `chunk`
+ * rows (the last one may be shorter) and each chunk runs through all
+ * iterations [L0, L1) of the block (as qg_loop_range on those rows) before
+ * the next chunk starts, so the FP16 scratch is sized for `chunk` rows, not
+ * M: scratch_bytes >= qg_loop_chunked_scratch_bytes(blk, M, chunk); after the
+ * call it holds the last chunk's intermediates.  chunk >= M is qg_loop_range.
+ * Rows do not interact in this block (its attention stand-in attends each row
+ * to itself), so each row's result is that of qg_loop_range on the chunk that
+ * holds it; it equals the single-shot result within the GEMM tolerance, and
+ * bit for bit where the chunk's tile plans match the single-shot M's.
+ * hcache: NULL, or the FP16-h cache (the pages' FP16-h KV mode keeps h and
+ * rebuilds K = W_k h and V = W_v h instead of storing K and V): FP16
+ * [L1 - L0][M][D], 16-byte aligned; iteration L0 + i of row r writes its
+ * attention input x = fp16(LN(h)), the QKV projection's input, at
+ * hcache[i][r][:].  qg_gemm_int4 / qg_gemm_int2 of cached x with the K (or
+ * V) rows of the QKV weight -- output channels [D, 2D) (or [2D, 3D)) of the
+ * N-major codes, scales and zeros, a contiguous row range -- rebuilds that
+ * iteration's K (V) columns of qkv, bit for bit where the GEMM's tile plan
+ * matches the QKV projection's.  Validation, stream order and the cached
+ * graphs (one per chunk) as in qg_loop_range. */
+int qg_loop_range_chunked(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
+                          int32_t chunk, void* scratch, size_t scratch_bytes, qg_half* hcache,
+                          void* stream);
+size_t qg_loop_chunked_scratch_bytes(const qg_block* blk, int32_t M, int32_t chunk);
 /* Byte offsets of norm, qkv, u, y and g inside the loop scratch (any pointer
  * may be NULL; g is 0 for a block without a gate).  Returns QG_EINVAL for a
  * bad block. */

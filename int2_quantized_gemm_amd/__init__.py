@@ -62,6 +62,8 @@ def _load():
         "qg_gemm_static_ws": (C.c_int, [vp, i64, W, vp, i64, i32, vp]),
         "qg_loop_range": (C.c_int, [B, vp, i32, i32, i32, vp, sz, vp]),
         "qg_loop_scratch_bytes": (sz, [B, i32]),
+        "qg_loop_range_chunked": (C.c_int, [B, vp, i32, i32, i32, i32, vp, sz, vp, vp]),
+        "qg_loop_chunked_scratch_bytes": (sz, [B, i32, i32]),
         "qg_loop_scratch_offsets": (C.c_int, [B, i32, C.POINTER(sz), C.POINTER(sz),
                                               C.POINTER(sz),
                                               C.POINTER(sz), C.POINTER(sz)]),
@@ -153,6 +155,15 @@ class PackedWeight:
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
+
+    def rows(self, n0: int, n1: int) -> "PackedWeight":
+        """Output channels [n0, n1) as a weight of their own: the N-major codes,
+        scales and zeros of a channel range are contiguous row ranges, so this
+        is a view (no copy); e.g. the K rows [D, 2D) of a QKV weight."""
+        if not 0 <= n0 < n1 <= self.N:
+            raise ValueError(f"rows [{n0}, {n1}) outside [0, {self.N})")
+        return PackedWeight(self.bits, self.K, n1 - n0, self.codes[n0:n1], self.scales[n0:n1],
+                            self.zeros[n0:n1], self.group)
 
 
 def qg_pack(W: torch.Tensor, bits: int, group: int = GROUP, out: PackedWeight | None = None,
@@ -300,6 +311,37 @@ def qg_loop_range(blk: Block, h: torch.Tensor, L0: int, L1: int,
                                               scratch.data_ptr(),
                                               scratch.numel() * scratch.element_size(),
                                               _stream(stream)))
+    return h
+
+
+def qg_loop_chunked_scratch_bytes(blk: Block, M: int, chunk: int) -> int:
+    b = blk.cstruct()
+    return lib.qg_loop_chunked_scratch_bytes(C.byref(b), M, chunk)
+
+
+def qg_loop_range_chunked(blk: Block, h: torch.Tensor, L0: int, L1: int, chunk: int,
+                          scratch: torch.Tensor | None = None, hcache: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """Chunk-first driver: rows of FP32 h [M][D] in chunks of `chunk`, each
+    through iterations [L0, L1) before the next (scratch sized for a chunk).
+    hcache: optional FP16 [L1 - L0][M][D] receiving each iteration's
+    attention input x (the FP16-h cache)."""
+    if h.dtype != torch.float32 or not h.is_contiguous() or h.dim() != 2 or h.shape[1] != blk.D:
+        raise ValueError(f"h must be a contiguous FP32 [M][{blk.D}] tensor, got "
+                         f"{tuple(h.shape)} {h.dtype}")
+    M = h.shape[0]
+    if hcache is not None and (hcache.dtype != torch.float16 or not hcache.is_contiguous()
+                               or tuple(hcache.shape) != (L1 - L0, M, blk.D)):
+        raise ValueError(f"hcache must be a contiguous FP16 [{L1 - L0}][{M}][{blk.D}] tensor")
+    if scratch is None:
+        scratch = torch.empty(max(qg_loop_chunked_scratch_bytes(blk, M, chunk), 256),
+                              dtype=torch.uint8, device=h.device)
+    b = blk.cstruct()
+    _check("qg_loop_range_chunked",
+           lib.qg_loop_range_chunked(C.byref(b), _dev(h, "h"), M, L0, L1, chunk,
+                                     scratch.data_ptr(), scratch.numel() * scratch.element_size(),
+                                     None if hcache is None else _dev(hcache, "hcache"),
+                                     _stream(stream)))
     return h
 
 

@@ -188,8 +188,12 @@ bool reduce_ln_fusion_enabled() {
 }
 
 // Enqueue `iters` iterations of the loop block on stream s (no validation).
+// hcache (optional): FP16 rows receiving each iteration's attention input
+// x = fp16(LN(h)), iteration l at hcache + l * hstride (the FP16-h cache:
+// the QKV GEMM then reads x from there instead of the norm scratch).
 hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
-                        const LoopLayout& L, bool fuse_swiglu, bool fuse_rln, hipStream_t s) {
+                        const LoopLayout& L, bool fuse_swiglu, bool fuse_rln, qg_half* hcache,
+                        int64_t hstride, hipStream_t s) {
     char* base = (char*)scratch;
     qg_half* norm = (qg_half*)(base + L.norm);
     qg_half* qkv = (qg_half*)(base + L.qkv);
@@ -217,6 +221,8 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
     // through the split-K reduction and the LayerNorm kernel instead, with
     // bit-identical results.
     const bool rln = M > 1 && qg::reduce_ln_supported(D);
+    // where iteration l's QKV input x is written and read
+    auto xbuf = [&](int32_t l) { return hcache ? hcache + (int64_t)l * hstride : norm; };
     auto residual_ln = [&](const qg_half* X, int64_t ldx, const qg_weight* w, qg_half* ln_out) {
         int parts = 0;
         qg::GemmArgs ra{X, ldx, w, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes};
@@ -231,11 +237,14 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
         return r;
     };
     for (int32_t l = 0; l < iters && e == hipSuccess; ++l) {
-        qg::GemmArgs qa{norm, D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws, L.ws_bytes};
-        if (fuse_qkv)
+        qg::GemmArgs qa{xbuf(l), D, &blk->qkv, qkv, 3 * D, M, qg::kStore, nullptr, 0, ws,
+                        L.ws_bytes};
+        if (fuse_qkv) {
             qa.ln_h = h;
-        else if (!(rln && l > 0))  // (else the previous down's launch wrote norm)
-            e = qg::launch_layernorm(h, M, D, norm, s);
+            qa.norm_out = hcache ? xbuf(l) : nullptr;
+        } else if (!(rln && l > 0)) {  // (else the previous down's launch wrote x)
+            e = qg::launch_layernorm(h, M, D, xbuf(l), s);
+        }
         if (e == hipSuccess) e = qg::launch_gemm(qa, s);
         if (e == hipSuccess && rln)
             e = residual_ln(qkv + 2 * D, 3 * D, &blk->out, norm);
@@ -269,7 +278,7 @@ hipError_t enqueue_loop(const qg_block* blk, float* h, int32_t M, int32_t iters,
             e = qg::launch_gemm(ua, s);
         }
         if (e == hipSuccess && rln)
-            e = residual_ln(u, F, &blk->down, l + 1 < iters ? norm : nullptr);
+            e = residual_ln(u, F, &blk->down, l + 1 < iters ? xbuf(l + 1) : nullptr);
         else if (e == hipSuccess)
             e = qg::launch_gemm({u, F, &blk->down, y, D, M, qg::kResidual, h, D, ws, L.ws_bytes},
                                 s);
@@ -290,6 +299,8 @@ struct LoopKey {
     qg_block blk;
     const float* h;
     void* scratch;
+    qg_half* hcache;
+    int64_t hstride;
     int32_t M, iters, device;
     bool fuse_swiglu, fuse_rln;
     bool operator==(const LoopKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
@@ -322,7 +333,7 @@ void sync_device(int device) {
 // so no other thread can evict (destroy) the graph between lookup and launch.
 hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t iters,
                              void* scratch, const LoopLayout& L, bool fuse_swiglu, bool fuse_rln,
-                             hipStream_t s) {
+                             qg_half* hcache, int64_t hstride, hipStream_t s) {
     LoopKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
     key.blk = *blk;
@@ -332,6 +343,8 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
     key.iters = iters;
     key.fuse_swiglu = fuse_swiglu;
     key.fuse_rln = fuse_rln;
+    key.hcache = hcache;
+    key.hstride = hcache ? hstride : 0;
     hipError_t e = hipGetDevice(&key.device);
     if (e != hipSuccess) return e;
     if (key.device < 0 || key.device >= 64) return hipErrorInvalidDevice;
@@ -348,7 +361,8 @@ hipError_t launch_loop_graph(const qg_block* blk, float* h, int32_t M, int32_t i
         return e;
     }
     if ((e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
-    hipError_t le = enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, fuse_rln, cs);
+    hipError_t le =
+        enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, fuse_rln, hcache, hstride, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {
@@ -625,6 +639,14 @@ size_t qg_loop_scratch_bytes(const qg_block* blk, int32_t M) {
     return loop_layout(blk, M).total;
 }
 
+size_t qg_loop_chunked_scratch_bytes(const qg_block* blk, int32_t M, int32_t chunk) {
+    if (!blk || M < 0 || chunk < 1 || blk->D <= 0 || blk->F <= 0) return 0;
+    if (M == 0) return 0;
+    const int32_t rows = chunk < M ? chunk : M, tail = M % rows;
+    const size_t a = loop_layout(blk, rows).total, b = tail ? loop_layout(blk, tail).total : 0;
+    return a > b ? a : b;
+}
+
 int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t* qkv, size_t* u,
                             size_t* y, size_t* g) {
     int st = check_block(blk, "qg_loop_scratch_offsets");
@@ -637,6 +659,25 @@ int qg_loop_scratch_offsets(const qg_block* blk, int32_t M, size_t* norm, size_t
     if (y) *y = L.y;
     if (g) *g = L.g;
     return ok();
+}
+
+// Iterations [L0, L1) on rows h [M][D] (validated), by the cached graph or,
+// under a caller's capture or with graphs off, kernel by kernel.
+static hipError_t run_loop(const qg_block* blk, float* h, int32_t M, int32_t iters, void* scratch,
+                           const LoopLayout& L, qg_half* hcache, int64_t hstride, hipStream_t s) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return e;
+    // Inside a caller's graph capture, or with graphs switched off, the
+    // kernels are enqueued one by one; otherwise the iteration sequence is
+    // replayed from a cached graph (one launch instead of 4-6 per iteration).
+    const bool fuse_swiglu = swiglu_fusion_enabled();
+    const bool fuse_rln = reduce_ln_fusion_enabled();
+    if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled())
+        return enqueue_loop(blk, h, M, iters, scratch, L, fuse_swiglu, fuse_rln, hcache, hstride,
+                            s);
+    return launch_loop_graph(blk, h, M, iters, scratch, L, fuse_swiglu, fuse_rln, hcache, hstride,
+                             s);
 }
 
 int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1, void* scratch,
@@ -655,21 +696,47 @@ int qg_loop_range(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t 
     if (scratch_bytes < L.total)
         return fail(QG_EINVAL, "%s: scratch of %zu bytes is smaller than the %zu required", fn,
                     scratch_bytes, L.total);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hipSuccess;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return hip_fail(fn, e);
-    // Inside a caller's graph capture, or with graphs switched off, the
-    // kernels are enqueued one by one; otherwise the iteration sequence is
-    // replayed from a cached graph (one launch instead of 4-6 per iteration).
-    const bool fuse_swiglu = swiglu_fusion_enabled();
-    const bool fuse_rln = reduce_ln_fusion_enabled();
-    if (cap != hipStreamCaptureStatusNone || !loop_graphs_enabled()) {
-        e = enqueue_loop(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, fuse_rln, s);
-    } else {
-        e = launch_loop_graph(blk, h, M, L1 - L0, scratch, L, fuse_swiglu, fuse_rln, s);
-    }
+    const hipError_t e = run_loop(blk, h, M, L1 - L0, scratch, L, nullptr, 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+int qg_loop_range_chunked(const qg_block* blk, float* h, int32_t M, int32_t L0, int32_t L1,
+                          int32_t chunk, void* scratch, size_t scratch_bytes, qg_half* hcache,
+                          void* stream) {
+    const char* fn = "qg_loop_range_chunked";
+    int st = check_block(blk, fn);
+    if (st) return st;
+    if (M < 0) return fail(QG_EINVAL, "%s: M = %d must be >= 0", fn, M);
+    if (chunk < 1) return fail(QG_EINVAL, "%s: chunk = %d must be >= 1", fn, chunk);
+    if (L0 < 0 || L1 < L0)
+        return fail(QG_EINVAL, "%s: need 0 <= L0 <= L1, got L0 = %d, L1 = %d", fn, L0, L1);
+    if (M == 0 || L0 == L1) return ok();
+    if (!h || !aligned(h, 16)) return fail(QG_EINVAL, "%s: h must be a 16-byte aligned pointer", fn);
+    if (hcache && !aligned(hcache, 16))
+        return fail(QG_EINVAL, "%s: hcache must be NULL or a 16-byte aligned pointer", fn);
+    const int32_t rows = chunk < M ? chunk : M;
+    const LoopLayout L = loop_layout(blk, rows);
+    const int32_t tail = M % rows;
+    const LoopLayout Lt = loop_layout(blk, tail ? tail : rows);
+    const size_t need = L.total > Lt.total ? L.total : Lt.total;
+    if (!scratch || !aligned(scratch, 256))
+        return fail(QG_EINVAL, "%s: scratch must be a 256-byte aligned pointer", fn);
+    if (scratch_bytes < need)
+        return fail(QG_EINVAL, "%s: scratch of %zu bytes is smaller than the %zu required for "
+                               "chunks of %d rows (qg_loop_chunked_scratch_bytes)", fn,
+                    scratch_bytes, need, rows);
+    // chunk first: rows [r0, r0 + m) run through all iterations before the
+    // next chunk starts; a ragged last chunk has a layout of its own
+    const int64_t D = blk->D;
+    for (int32_t r0 = 0; r0 < M; r0 += rows) {
+        const int32_t m = M - r0 < rows ? M - r0 : rows;
+        const LoopLayout& Lc = m == rows ? L : Lt;
+        const hipError_t e = run_loop(blk, h + (int64_t)r0 * D, m, L1 - L0, scratch, Lc,
+                                      hcache ? hcache + (int64_t)r0 * D : nullptr,
+                                      (int64_t)M * D, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(fn, e);
+    }
     return ok();
 }
 

@@ -290,3 +290,35 @@ def test_static_ws_rejects_bad_weight(kw, code, needle):
 def test_static_ws_rejects_bad_operands(kw, needle):
     assert _gemm_static(_w(), **kw) == qg.QG_EINVAL
     assert needle in qg.qg_last_error()
+
+
+def _block_struct(D=256, F=512):
+    w = lambda K, N: _w(bits=4, K=K, N=N)
+    g = qg._Weight(0, 0, 0, 0, None, None, None)
+    return qg._Block(D, F, w(D, 3 * D), w(D, D), w(D, F), w(F, D), g)
+
+
+def test_chunked_scratch_bytes():
+    """The chunked driver's scratch covers a full chunk and the ragged tail,
+    and is no larger than a single shot's once chunks are smaller than M."""
+    b = _block_struct(2048, 8192)
+    one = lambda M: qg.lib.qg_loop_scratch_bytes(C.byref(b), M)
+    ch = lambda M, c: qg.lib.qg_loop_chunked_scratch_bytes(C.byref(b), M, c)
+    assert ch(2048, 512) == one(512) < one(2048)
+    assert ch(1100, 512) >= max(one(512), one(76))
+    assert ch(300, 4096) == one(300)
+    assert ch(0, 512) == 0 and ch(10, 0) == 0
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(chunk=0), "chunk"), (dict(scratch_bytes=100), "smaller"), (dict(hcache=FAKE + 2), "hcache"),
+    (dict(L0=3, L1=2), "L0"), (dict(h=FAKE + 4), "h must"),
+])
+def test_chunked_rejects_bad_arguments(kw, needle):
+    b = _block_struct()
+    a = dict(h=FAKE, M=40, L0=0, L1=2, chunk=16, scratch=FAKE, scratch_bytes=1 << 30, hcache=None)
+    a.update(kw)
+    st = qg.lib.qg_loop_range_chunked(C.byref(b), a["h"], a["M"], a["L0"], a["L1"], a["chunk"],
+                                      a["scratch"], a["scratch_bytes"], a["hcache"], None)
+    assert st == qg.QG_EINVAL
+    assert needle in qg.qg_last_error()
