@@ -12,8 +12,12 @@
  *
  * Packed format, layout version 1 (b = bits in {4, 2}, G = group = 128 or K,
  * g = k / G):
- *   - codes:  uint32 [N][K*b/32], row n = output channel n, contiguous along K
- *             (INT4 rows are K/2 bytes, INT2 rows K/4 bytes).  Inside a word,
+ *   - codes:  uint32 rows, row n = output channel n, contiguous along K
+ *             (INT4 rows hold K/2 bytes, INT2 rows K/4 bytes), row n starting
+ *             at word n * ldc (ldc = K*b/32 for compact rows; a larger ldc
+ *             leaves the words past K*b/32 of each row unused, e.g. INT2 rows
+ *             kept at the INT4 row stride after an in-place re-quantisation,
+ *             CTX-TIER "Details of the shipped kernel").  Inside a word,
  *             code j (j = k mod 32/b) sits at bit 16*(j mod 2) + b*floor(j/2):
  *             even codes in the low half-word, odd codes in the high half-word.
  *   - scales: FP16 [N][K/G];  zeros: FP16 [N][K/G], integer values in
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 2
+#define QG_ABI_VERSION 3
 #define QG_LAYOUT_VERSION 1
 
 /* Status codes.  EINVAL: bad argument (the pages' ValueError); EUNSUPPORTED:
@@ -67,7 +71,9 @@ typedef uint16_t qg_half; /* IEEE binary16 bit pattern */
 /* One packed weight (the pages' QuantWeight: packed data, FP16 scales and
  * zeros, bits; CTX-TIER Phase 2).  bits in {4, 2}; group == 128 or group == K
  * (per-row: scales and zeros are [N][1]); K % 128 == 0 and K <= 2^22; N >= 1;
- * codes 16-byte aligned; scales/zeros 2-byte aligned. */
+ * codes 16-byte aligned; scales/zeros 2-byte aligned.  ldc: uint32 words
+ * from one code row to the next; 0 means compact rows (K*bits/32), otherwise
+ * at least K*bits/32, a multiple of 4 (16-byte rows) and at most 2^20. */
 typedef struct qg_weight {
     int32_t bits;
     int32_t K;
@@ -76,6 +82,7 @@ typedef struct qg_weight {
     const uint32_t* codes;
     const qg_half* scales;
     const qg_half* zeros;
+    int64_t ldc;
 } qg_weight;
 
 /* The looped block's weights: qkv K=D, N=3D; out K=D, N=D; up K=D, N=F;
@@ -106,7 +113,8 @@ const char* qg_last_error(void);
 /* Quantise FP32 W [K][ldw] (ldw >= N) into layout v1 (see the format above;
  * CTX-TIER kernel details: per-group asymmetric scale = range / (levels - 1)).
  * group: 128, or K for per-row groups (QG_EUNSUPPORTED otherwise).
- * codes [N][K*bits/32], scales and zeros [N][K/group] are written in full.
+ * codes [N][K*bits/32] (compact rows), scales and zeros [N][K/group] are
+ * written in full.
  * Bit-identical to the definition (FP64 arithmetic on the device).
  * Runs in two passes on `stream`: a validation pass that computes every
  * group's range and scale and writes nothing (no output at all), then, after
@@ -123,12 +131,17 @@ int qg_pack(const float* W, int64_t ldw, int32_t K, int32_t N, int32_t bits, int
  * INT4 dequant (q - z) s goes through qg_pack's quantiser with bits = 2; the
  * result is bit-identical to that definition.
  * w4: bits 4; w2: bits 2, same K, N and group; both described like any
- * qg_weight (w2's codes are compact, [N][K/16]).  Per-row groups (group == K)
- * need K <= 32768 (QG_EUNSUPPORTED otherwise).  Out of place, w2's buffers must not
- * overlap w4's or each other.  In place: w2->codes == w4->codes writes the
- * INT2 codes compactly over the first half of the INT4 code buffer (the rest
- * is left as it was), and w2->scales == w4->scales / w2->zeros == w4->zeros
- * overwrite those arrays; any other overlap is QG_EINVAL.  Runs in two
+ * qg_weight, each with its own row stride.  Per-row groups (group == K)
+ * need K <= 32768 (QG_EUNSUPPORTED otherwise).  Out of place, w2's buffers
+ * must not overlap w4's or each other.  In place (w2->codes == w4->codes,
+ * w2->scales == w4->scales, w2->zeros == w4->zeros; any other overlap is
+ * QG_EINVAL), two forms: with w2's row stride equal to w4's -- the pages'
+ * in-place mode, INT2 rows kept at the INT4 stride (K/2 bytes), each INT2 row
+ * over the front half of its own INT4 row -- one launch for groups of 128 up
+ * to K = 32768 (beyond that one launch per doubling of the group index), and
+ * with compact w2 rows (K/4 bytes), written over the first half of the INT4
+ * buffer, which takes launches ordered by row (about log2 of the rows and of
+ * the groups); the bytes past the INT2 data are left as they were.  Runs in two
  * passes on `stream`, like qg_pack: a validation pass that writes nothing,
  * then, after synchronising `stream` to read its verdict, the re-quantisation.
  * A non-finite INT4 scale or zero, or an INT2 scale that overflows FP16,

@@ -34,7 +34,8 @@ class QGValueError(QGError, ValueError):
 
 class _Weight(C.Structure):
     _fields_ = [("bits", C.c_int32), ("K", C.c_int32), ("N", C.c_int32), ("group", C.c_int32),
-                ("codes", C.c_void_p), ("scales", C.c_void_p), ("zeros", C.c_void_p)]
+                ("codes", C.c_void_p), ("scales", C.c_void_p), ("zeros", C.c_void_p),
+                ("ldc", C.c_int64)]
 
 
 class _Block(C.Structure):
@@ -115,9 +116,11 @@ def qg_last_error() -> str:
 
 @dataclass
 class PackedWeight:
-    """Layout-v1 packed weight: codes int32 [N][K*bits/32] (uint32 bit
-    patterns), scales/zeros float16 [N][K/group]; group 128, or K for per-row
-    groups (one scale and zero per output channel)."""
+    """Layout-v1 packed weight: codes int32 [N][>= K*bits/32] (uint32 bit
+    patterns; each row's first K*bits/32 words hold its codes, rows
+    codes.stride(0) words apart -- more than K*bits/32 for INT2 rows kept at
+    the INT4 stride), scales/zeros float16 [N][K/group]; group 128, or K for
+    per-row groups (one scale and zero per output channel)."""
     bits: int
     K: int
     N: int
@@ -129,18 +132,22 @@ class PackedWeight:
     def cstruct(self) -> _Weight:
         # the C side sees only pointers: the tensors must hold what bits, K,
         # N and group say
-        if (tuple(self.codes.shape) != (self.N, self.K * self.bits // 32)
-                or self.codes.element_size() != 4 or not self.codes.is_contiguous()):
-            raise ValueError(f"codes must be a contiguous 32-bit [{self.N}][{self.K * self.bits // 32}]"
-                             f" tensor, got {tuple(self.codes.shape)} {self.codes.dtype}")
+        words = self.K * self.bits // 32
+        if (self.codes.dim() != 2 or self.codes.shape[0] != self.N or self.codes.shape[1] < words
+                or self.codes.element_size() != 4 or self.codes.stride(1) != 1
+                or self.codes.stride(0) < words):
+            raise ValueError(f"codes must be a 32-bit [{self.N}][>= {words}] tensor with unit column "
+                             f"stride, got {tuple(self.codes.shape)} {self.codes.dtype} strides "
+                             f"{self.codes.stride()}")
         groups = self.K // self.group if self.group else 0
         for name, t in (("scales", self.scales), ("zeros", self.zeros)):
             if (tuple(t.shape) != (self.N, groups) or t.dtype != torch.float16
                     or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous FP16 [{self.N}][{groups}] tensor, "
                                  f"got {tuple(t.shape)} {t.dtype}")
+        ldc = self.codes.stride(0) if self.N > 1 else words
         return _Weight(self.bits, self.K, self.N, self.group, self.codes.data_ptr(),
-                       self.scales.data_ptr(), self.zeros.data_ptr())
+                       self.scales.data_ptr(), self.zeros.data_ptr(), 0 if ldc == words else ldc)
 
     @staticmethod
     def empty(K: int, N: int, bits: int, device="cuda", group: int = GROUP) -> "PackedWeight":
@@ -154,7 +161,10 @@ class PackedWeight:
                             group)
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
+        """Bytes the weight holds: its codes (K*bits/8 a row, row padding not
+        counted), scales and zeros."""
+        return (self.N * self.K * self.bits // 8
+                + sum(t.numel() * t.element_size() for t in (self.scales, self.zeros)))
 
     def rows(self, n0: int, n1: int) -> "PackedWeight":
         """Output channels [n0, n1) as a weight of their own: the N-major codes,
@@ -366,25 +376,30 @@ def qg_release_cache() -> None:
 
 
 def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place: bool = False,
-                    stream=None) -> PackedWeight:
+                    compact: bool = False, stream=None) -> PackedWeight:
     """INT4 -> INT2 re-quantisation on the GPU: a validation pass (which
     synchronises the stream and raises, with nothing written, on a non-finite
     INT4 scale or zero or an overflowing INT2 scale), then the re-quantisation,
     enqueued on the stream.
 
-    Out of place the result goes to `out` (or new tensors).  With
-    in_place=True the INT2 codes are written compactly over the front of
-    w4.codes and the INT2 scales/zeros over w4's: the returned weight views
-    w4's memory, and w4 no longer holds INT4 data."""
+    Out of place the result goes to `out` (or new compact tensors).  With
+    in_place=True the INT2 weight takes over w4's memory (codes, scales and
+    zeros): its rows keep the INT4 row stride (K/2 bytes, each INT2 row over
+    the front half of its INT4 row; one launch), or with compact=True they are
+    packed K/4 bytes apart over the front of the INT4 buffer.  The returned
+    weight views w4's memory, and w4 no longer holds INT4 data."""
     if w4.bits != 4:
         raise ValueError("w4 must be an INT4 weight")
     K, N = w4.K, w4.N
     if in_place:
         if out is not None:
             raise ValueError("in_place and out are exclusive")
-        if not w4.codes.is_contiguous():
-            raise ValueError("in place needs contiguous INT4 codes")
-        codes = w4.codes.view(-1)[:N * (K // 16)].view(N, K // 16)
+        if compact:
+            if not w4.codes.is_contiguous():
+                raise ValueError("compact in place needs contiguous INT4 codes")
+            codes = w4.codes.view(-1)[:N * (K // 16)].view(N, K // 16)
+        else:
+            codes = w4.codes
         out = PackedWeight(2, K, N, codes, w4.scales, w4.zeros, w4.group)
     elif out is None:
         out = PackedWeight.empty(K, N, 2, w4.codes.device, w4.group)
@@ -393,13 +408,13 @@ def qg_requant_4to2(w4: PackedWeight, out: PackedWeight | None = None, in_place:
     return out
 
 
-def requant_block(blk: Block, in_place: bool = False, stream=None) -> Block:
+def requant_block(blk: Block, in_place: bool = False, compact: bool = False, stream=None) -> Block:
     """The INT4 -> INT2 tier switch of a loop block ("β-Informed Deployment
     Features" page, CTX-TIER apply step): re-quantise each INT4 projection
     (INT2 ones are kept).  The re-quantisations are enqueued on the stream;
     torch's allocator is stream-ordered, so the INT4 tensors may be dropped
     (out of place) as soon as the caller releases `blk`."""
-    ws = {k: qg_requant_4to2(w, in_place=in_place, stream=stream) if w.bits == 4 else w
+    ws = {k: qg_requant_4to2(w, in_place=in_place, compact=compact, stream=stream) if w.bits == 4 else w
           for k, w in blk.weights().items()}
     return Block(blk.D, blk.F, ws["qkv"], ws["out"], ws["up"], ws["down"], ws.get("gate"))
 

@@ -17,6 +17,10 @@ inline SzIdx sz_idx(const qg_weight& w) {
     return w.group == kGroup ? SzIdx{w.K / kGroup, 1} : SzIdx{1, 0};
 }
 inline bool per_row(const qg_weight& w) { return w.group != kGroup; }
+// Row stride of a validated weight's codes, in uint32 words.
+inline int64_t code_ld(const qg_weight& w) {
+    return w.ldc ? w.ldc : (int64_t)w.K * w.bits / 32;
+}
 
 // ---- pack / unpack / dequant (kernels_pack.hip)
 // Pack and re-quantisation run in two passes.  The validation pass writes
@@ -30,6 +34,8 @@ hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int 
                        uint32_t* codes, qg_half* scales, qg_half* zeros, hipStream_t s);
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s);
 hipError_t launch_requant_4to2_check(const qg_weight& w4, int* status, int tag, hipStream_t s);
+// in_place: w2 aliases w4 (codes, scales, zeros); the INT2 rows keep w2's
+// row stride (w4's for the pages' in-place form, compact otherwise).
 hipError_t launch_requant_4to2(const qg_weight& w4, const qg_weight& w2, bool in_place,
                                hipStream_t s);
 // Largest K the per-row re-quantisation holds in one workgroup's registers.

@@ -90,8 +90,8 @@ constexpr int kSkinnyPairMinWgs = 192;
 template <int BITS, int NT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz, int K,
-    int N, int S, OutEpi out, float* __restrict__ part) {
+    int64_t ldc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz,
+    int K, int N, int S, OutEpi out, float* __restrict__ part) {
     static_assert(NT == 1 || NT == 2, "one or two column tiles (wave t stores tile t)");
     constexpr int kMaxGpw = kSkinnyMaxK / kGroup / 4;  // groups per wave
     __shared__ __attribute__((aligned(1024))) uint8_t xs[16 * kSkinnyMaxK * 2];
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         const int n = (blockIdx.x * NT + t) * 16 + nl;
         const bool nvalid = n < N;
         const int nr = nvalid ? n : N - 1;
-        const uint32_t* crow = codes + (int64_t)nr * (K / Fmt<BITS>::kCodesPerWord);
+        const uint32_t* crow = codes + (int64_t)nr * ldc;
 #pragma unroll
         for (int i = 0; i < kMaxGpw; ++i) {
             const int gi = wave + 4 * i;
@@ -216,11 +216,13 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     const int pairs = (a.w->N + 31) / 32;
     if ((int64_t)pairs * S >= kSkinnyPairMinWgs)
         k_gemm_skinny<BITS, 2><<<dim3(pairs, S), 256, 0, s>>>(
-            a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N, S,
+            a.X, a.ldx, a.M, a.w->codes, code_ld(*a.w), a.w->scales, a.w->zeros, sz_idx(*a.w),
+            a.w->K, a.w->N, S,
             a.out(), part);
     else
         k_gemm_skinny<BITS, 1><<<dim3((a.w->N + 15) / 16, S), 256, 0, s>>>(
-            a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N, S,
+            a.X, a.ldx, a.M, a.w->codes, code_ld(*a.w), a.w->scales, a.w->zeros, sz_idx(*a.w),
+            a.w->K, a.w->N, S,
             a.out(), part);
     hipError_t e = hipGetLastError();
     if (a.parts) *a.parts = S;

@@ -115,7 +115,8 @@ struct GemvWeights {
     const uint32_t* codes[2];
     const uint16_t* scales[2];
     const uint16_t* zeros[2];
-    SzIdx sz;  // scale addressing, the same for both weights
+    int64_t ldc[2];  // code row strides (words)
+    SzIdx sz;        // scale addressing, the same for both weights
 };
 
 template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
@@ -130,7 +131,6 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     constexpr int WPL = G::WPL;
     constexpr int PAIRS = G::PAIRS;  // FP16 pairs of x per lane and chunk
     constexpr int K = 32 * LPR * CPR;
-    constexpr int wpr = K / F::kCodesPerWord;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int sub = lane % LPR;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
                 const int wi = (c * LPR + sub) * WPL;
-                wv[b][u][c] = *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * wpr + wi);
+                wv[b][u][c] = *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * W.ldc[b] + wi);
                 const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
                 sv[b][u][c] = W.scales[b][sg];
                 zv[b][u][c] = W.zeros[b][sg];
@@ -341,7 +341,7 @@ hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
     const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     const qg_weight* w1 = NW == 2 ? a.w2 : a.w;
     const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros},
-                        sz_idx(*a.w)};
+                        {code_ld(*a.w), code_ld(*w1)}, sz_idx(*a.w)};
     k_gemv<BITS, LPR, CPR, U, LN, NW><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
         a.X, a.ln_h, a.norm_out, W, N, a.out(), a.g_out);
     return hipGetLastError();

@@ -76,14 +76,16 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ W, int64
     }
 }
 
-// One thread per packed word: writes the word's codes q[n][k] as bytes.
+// One thread per packed word (i = n * wpr + word of row n, wpr = K*b/32,
+// rows ldc words apart in memory): writes the word's codes q[n][k] as bytes.
 template <int BITS>
-__global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ codes, int64_t words,
+__global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ codes, int64_t wpr,
+                                                int64_t ldc, int64_t words,
                                                 uint8_t* __restrict__ q) {
     using F = Fmt<BITS>;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= words) return;
-    const uint32_t w = codes[i];
+    const uint32_t w = codes[(i / wpr) * ldc + i % wpr];
     uint8_t* o = q + i * F::kCodesPerWord;
 #pragma unroll
     for (int p = 0; p < F::kPairsPerWord; ++p) {
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ cod
 // One thread per packed word: writes w^[n][k] for the word's codes, FP32
 // (exact) or FP16 (one rounding), with the GEMM kernels' dequant helpers.
 template <int BITS, bool F16OUT>
-__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes, int64_t ldc,
                                                  const uint16_t* __restrict__ scales,
                                                  const uint16_t* __restrict__ zeros, SzIdx sz,
                                                  int K, int64_t words, void* __restrict__ out) {
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
     const int64_t g = (i % wpr) / F::kWordsPerGroup;
     const int64_t sg = sz.at(n, g);
     const GroupConst c = group_const(scales[sg], zeros[sg]);
-    const uint32_t w = codes[i];
+    const uint32_t w = codes[n * ldc + i % wpr];
     const int64_t k0 = i * F::kCodesPerWord;  // == n*K + (i % wpr) * codes/word
 #pragma unroll
     for (int p = 0; p < F::kPairsPerWord; ++p) {
@@ -158,10 +160,11 @@ hipError_t launch_pack(const float* W, int64_t ldw, int K, int N, int bits, int 
 hipError_t launch_unpack(const qg_weight& w, uint8_t* q, hipStream_t s) {
     const int64_t words = (int64_t)w.N * (w.K * w.bits / 32);
     const int64_t blocks = (words + 255) / 256;
+    const int64_t wpr = w.K * w.bits / 32;
     if (w.bits == 4)
-        k_unpack<4><<<(unsigned)blocks, 256, 0, s>>>(w.codes, words, q);
+        k_unpack<4><<<(unsigned)blocks, 256, 0, s>>>(w.codes, wpr, code_ld(w), words, q);
     else
-        k_unpack<2><<<(unsigned)blocks, 256, 0, s>>>(w.codes, words, q);
+        k_unpack<2><<<(unsigned)blocks, 256, 0, s>>>(w.codes, wpr, code_ld(w), words, q);
     return hipGetLastError();
 }
 
@@ -171,14 +174,14 @@ hipError_t launch_dequant(const qg_weight& w, bool fp16, void* out, hipStream_t 
     const unsigned blocks = (unsigned)((words + 255) / 256);
     if (w.bits == 4) {
         if (fp16)
-            k_dequant<4, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
+            k_dequant<4, true><<<blocks, 256, 0, s>>>(w.codes, code_ld(w), w.scales, w.zeros, sz, w.K, words, out);
         else
-            k_dequant<4, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
+            k_dequant<4, false><<<blocks, 256, 0, s>>>(w.codes, code_ld(w), w.scales, w.zeros, sz, w.K, words, out);
     } else {
         if (fp16)
-            k_dequant<2, true><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
+            k_dequant<2, true><<<blocks, 256, 0, s>>>(w.codes, code_ld(w), w.scales, w.zeros, sz, w.K, words, out);
         else
-            k_dequant<2, false><<<blocks, 256, 0, s>>>(w.codes, w.scales, w.zeros, sz, w.K, words, out);
+            k_dequant<2, false><<<blocks, 256, 0, s>>>(w.codes, code_ld(w), w.scales, w.zeros, sz, w.K, words, out);
     }
     return hipGetLastError();
 }

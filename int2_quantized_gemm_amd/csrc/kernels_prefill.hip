@@ -85,8 +85,8 @@ template <int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int ST
           int STORE_FROM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefill(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz, int K,
-    int N, OutEpi out, int groups_per_part, float* __restrict__ part) {
+    int64_t ldc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, SzIdx sz,
+    int K, int N, OutEpi out, int groups_per_part, float* __restrict__ part) {
     using C = Cfg<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES>;
     __shared__ __attribute__((aligned(16))) f16 lds[C::LDS_HALVES];
 
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
     const int l32 = lane & 31, hh = lane >> 5;
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
-    const int wpr = K / Fmt<BITS>::kCodesPerWord;
+    const int wpr = (int)ldc;  // code row stride in words (<= 2^20)
     // K split: workgroup z covers groups [g_lo, g_lo + groups_per_part) and,
     // when `part` is set, writes its FP32 partial tile to part[z][M][N].
     const int g_lo = blockIdx.z * groups_per_part;
@@ -396,8 +396,8 @@ __device__ __forceinline__ void for_each_index(Fn&& f, std::integer_sequence<int
 template <int BITS, int BM, int RA, int RBS, int SZ>
 __global__ __launch_bounds__(256) void k_gemm_ring(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K, int N,
-    OutEpi out, int groups_per_part, float* __restrict__ part, Raster rs) {
+    int64_t ldc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K,
+    int N, OutEpi out, int groups_per_part, float* __restrict__ part, Raster rs) {
     using F = Fmt<BITS>;
     using RB = RingB<BITS>;
     constexpr int TM = BM / 32;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     const int m0 = ty * BM;
     const int n0 = tx * 128;
     const int groups = K / kBK;
-    const int wpr = K / F::kCodesPerWord;
+    const int wpr = (int)ldc;  // code row stride in words (<= 2^20)
     const int g_lo = blockIdx.z * groups_per_part;
     const int G = groups_per_part;
 
@@ -762,8 +762,8 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     constexpr int threads = 64 * WAVES_M * WAVES_N * KSPLIT;
     float* part = split > 1 || a.parts ? (float*)a.ws : nullptr;
     k_gemm_prefill<BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, STAGES, STORE_FROM><<<grid, threads, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, sz_idx(*a.w), a.w->K, a.w->N,
-        a.out(), a.w->K / kBK / split, part);
+        a.X, a.ldx, a.M, a.w->codes, code_ld(*a.w), a.w->scales, a.w->zeros, sz_idx(*a.w),
+        a.w->K, a.w->N, a.out(), a.w->K / kBK / split, part);
     hipError_t e = hipGetLastError();
     if (a.parts) *a.parts = split;
     if (e != hipSuccess || split == 1 || a.parts) return e;
@@ -779,8 +779,8 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
     float* part = split > 1 || a.parts ? (float*)a.ws : nullptr;
     k_gemm_ring<BITS, BM, RA, RBS, SZ><<<grid, 256, 0, s>>>(
-        a.X, a.ldx, a.M, a.w->codes, a.w->scales, a.w->zeros, a.w->K, a.w->N, a.out(),
-        a.w->K / kBK / split, part, rs);
+        a.X, a.ldx, a.M, a.w->codes, code_ld(*a.w), a.w->scales, a.w->zeros, a.w->K, a.w->N,
+        a.out(), a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
     if (a.parts) *a.parts = split;
     if (e != hipSuccess || split == 1 || a.parts) return e;

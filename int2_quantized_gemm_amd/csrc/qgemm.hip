@@ -70,6 +70,11 @@ int check_weight(const qg_weight* w, const char* fn, const char* name) {
         return fail(QG_EINVAL, "%s: %s.codes must be 16-byte aligned", fn, name);
     if (!aligned(w->scales, 2) || !aligned(w->zeros, 2))
         return fail(QG_EINVAL, "%s: %s.scales/zeros must be 2-byte aligned", fn, name);
+    const int64_t compact = (int64_t)w->K * w->bits / 32;
+    if (w->ldc != 0 && (w->ldc < compact || w->ldc % 4 != 0 || w->ldc > (int64_t(1) << 20)))
+        return fail(QG_EINVAL, "%s: %s.ldc = %lld must be 0 (compact) or a multiple of 4 in "
+                               "[K*bits/32 = %lld, 2^20]", fn, name, (long long)w->ldc,
+                    (long long)compact);
     return QG_OK;
 }
 
@@ -547,7 +552,10 @@ int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
         return fail(QG_EUNSUPPORTED, "%s: per-row groups need K <= %d (K = %d)", fn,
                     qg::kRequantRowMaxK, w4->K);
     const int groups = w4->K / w4->group;
-    const size_t c4 = (size_t)w4->N * (w4->K / 8) * 4, c2 = (size_t)w4->N * (w4->K / 16) * 4;
+    const int64_t l4 = qg::code_ld(*w4), l2 = qg::code_ld(*w2);
+    // bytes each code array spans: N - 1 strides and one row
+    const size_t c4 = ((size_t)(w4->N - 1) * l4 + w4->K / 8) * 4;
+    const size_t c2 = ((size_t)(w4->N - 1) * l2 + w4->K / 16) * 4;
     const size_t sz = (size_t)w4->N * groups * 2;
     const void* in[3] = {w4->codes, w4->scales, w4->zeros};
     const size_t in_bytes[3] = {c4, sz, sz};
@@ -569,6 +577,10 @@ int qg_requant_4to2(const qg_weight* w4, const qg_weight* w2, void* stream) {
                 return fail(QG_EINVAL, "%s: the outputs overlap each other", fn);
     }
     const bool in_place = w2->codes == w4->codes;
+    if (in_place && l2 != l4 && l2 != w4->K / 16)
+        return fail(QG_EINVAL, "%s: in place, w2.ldc must give w4's row stride (%lld words) or "
+                               "compact rows (%d words), got %lld", fn, (long long)l4, w4->K / 16,
+                    (long long)l2);
     hipStream_t s = (hipStream_t)stream;
     std::lock_guard<std::mutex> lock(g_pack_mu);
     int bad = 0;

@@ -94,12 +94,9 @@ static int run_loop(const char* in_path, const char* out_path) {
         QG_OK_(qg_pack(dW, N, K, N, 4, 128, codes, scales, zeros, s));
         w[i] = {4, K, N, 128, codes, scales, zeros};
         if (bits == 2) {
-            uint32_t* codes2;
-            qg_half *scales2, *zeros2;
-            HIP_OK(dev.alloc(&codes2, (size_t)N * K / 16 * 4));
-            HIP_OK(dev.alloc(&scales2, nsz * 2));
-            HIP_OK(dev.alloc(&zeros2, nsz * 2));
-            const qg_weight w2 = {2, K, N, 128, codes2, scales2, zeros2};
+            // the tier switch in place, INT2 rows kept at the INT4 row stride
+            // (K/8 words): the pages' in-place form, through the ldc field
+            const qg_weight w2 = {2, K, N, 128, codes, scales, zeros, (int64_t)K / 8};
             QG_OK_(qg_requant_4to2(&w[i], &w2, s));
             w[i] = w2;
         }

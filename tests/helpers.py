@@ -30,9 +30,15 @@ def assert_close(a, ref, what: str, max_abs: float = MAX_ABS, rel: float = REL_L
     return e, m
 
 
+def compact_codes(p) -> np.ndarray:
+    """The codes of a PackedWeight as compact uint32 rows [N][K*bits/32]
+    (rows kept at a larger stride give their first K*bits/32 words)."""
+    return np.ascontiguousarray(p.codes[:, :p.K * p.bits // 32].cpu().numpy().view(np.uint32))
+
+
 def to_oracle(p, orc):
     """PackedWeight (GPU) -> oracle.Packed, for comparisons of outputs only."""
-    return orc.Packed(p.bits, p.K, p.N, p.codes.cpu().numpy().view(np.uint32).copy(),
+    return orc.Packed(p.bits, p.K, p.N, compact_codes(p),
                       p.scales.cpu().numpy().view(np.uint16).copy(),
                       p.zeros.cpu().numpy().view(np.uint16).copy())
 

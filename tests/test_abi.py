@@ -29,10 +29,10 @@ def test_header_functions_are_exported():
 
 
 def test_versions():
-    assert qg.qg_abi_version() == 2
+    assert qg.qg_abi_version() == 3
     assert qg.qg_layout_version() == 1
     text = open(HEADER).read()
-    assert "#define QG_ABI_VERSION 2" in text and "#define QG_LAYOUT_VERSION 1" in text
+    assert "#define QG_ABI_VERSION 3" in text and "#define QG_LAYOUT_VERSION 1" in text
 
 
 def _w(bits=4, K=2048, N=2048, group=128, codes=FAKE, scales=FAKE, zeros=FAKE):
@@ -322,3 +322,19 @@ def test_chunked_rejects_bad_arguments(kw, needle):
                                       a["scratch"], a["scratch_bytes"], a["hcache"], None)
     assert st == qg.QG_EINVAL
     assert needle in qg.qg_last_error()
+
+
+@pytest.mark.parametrize("ldc,ok", [(0, True), (256, True), (260, True), (1 << 20, True),
+                                    (255, False), (258, False), (60, False), (102, False),
+                                    ((1 << 20) + 4, False)])
+def test_weight_code_row_stride(ldc, ok):
+    """ldc: 0 (compact) or a multiple of 4 words in [K*bits/32, 2^20]; a good
+    stride passes the weight check and the call stops at the next operand
+    check (ldy too small), before any launch."""
+    w = _w(bits=4, K=512, N=64)  # compact rows: 64 words
+    w.ldc = ldc if ldc != 256 else 64
+    st = _gemm(qg.lib.qg_gemm_int4, w, ldx=512, ldy=8)
+    assert st == qg.QG_EINVAL
+    assert ("ldy" in qg.qg_last_error()) == ok, qg.qg_last_error()
+    if not ok:
+        assert "ldc" in qg.qg_last_error()

@@ -295,3 +295,43 @@ def test_gemm_captured_in_graph_replays(M):
         assert np.array_equal(f16_bits(Y), ref), f"replay {r}"
         qg.qg_gemm_int4(Xd[:1], p)
         torch.cuda.synchronize()
+
+
+def _strided(p, pad_words):
+    """The same weight with its code rows pad_words (a multiple of 4) apart
+    past K*bits/32, the padding filled with a pattern no row should read."""
+    words = p.K * p.bits // 32
+    buf = torch.full((p.N, words + pad_words), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    buf[:, :words] = p.codes
+    return qg.PackedWeight(p.bits, p.K, p.N, buf, p.scales, p.zeros, p.group)
+
+
+# Every kernel route with code rows at a larger stride (ldc): the GEMV, the
+# skinny kernel (with K parts), the 32-, 64- and 128-row ring tiles (with a K
+# split), the staged kernel (K of 10 groups) -- bit for bit against the same
+# weight with compact rows.
+STRIDED = [(1, 2048, 304), (1, 8192, 64), (9, 6144, 40), (40, 2048, 520), (300, 2048, 2104),
+           (2048, 8192, 2048), (200, 1280, 296), (64, 8192, 256)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("M,K,N", STRIDED)
+def test_gemm_code_row_stride(orc, bits, M, K, N):
+    W, X = workloads.single_gemm(M, K, N, seed=M + K + N + 5)
+    p = qg.qg_pack(W.cuda(), bits)
+    Xd = X.cuda()
+    ref = f16_bits(GEMM[bits](Xd, p))
+    for pad in (4, K * bits // 32):  # one extra 16-byte chunk; INT4-stride INT2 rows
+        got = f16_bits(GEMM[bits](Xd, _strided(p, pad)))
+        assert np.array_equal(got, ref), f"bits={bits} M={M} K={K} N={N} pad={pad}"
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_unpack_and_dequant_code_row_stride(bits):
+    W, _ = workloads.single_gemm(1, 512, 33, seed=77)
+    p = qg.qg_pack(W.cuda(), bits)
+    s = _strided(p, 8)
+    assert torch.equal(qg.qg_unpack(s), qg.qg_unpack(p))
+    assert torch.equal(qg.qg_dequant(s), qg.qg_dequant(p))
+    assert torch.equal(qg.qg_dequant(s, fp16=True).view(torch.int16),
+                       qg.qg_dequant(p, fp16=True).view(torch.int16))

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import Guarded, assert_close, f16_bits
+from helpers import Guarded, assert_close, compact_codes, f16_bits
 
 qg = pytest.importorskip("int2_quantized_gemm_amd")
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,7 @@ GEMM = {4: qg.qg_gemm_int4, 2: qg.qg_gemm_int2}
 
 def _same(p, op, what):
     assert p.group == op.group == p.K, what
-    assert np.array_equal(p.codes.cpu().numpy().view(np.uint32), op.codes), f"{what}: codes"
+    assert np.array_equal(compact_codes(p), op.codes), f"{what}: codes"
     assert np.array_equal(f16_bits(p.scales), op.scales), f"{what}: scales"
     assert np.array_equal(f16_bits(p.zeros), op.zeros), f"{what}: zeros"
 
@@ -73,17 +73,22 @@ def test_perrow_gemm_paths(orc, bits, M, K, N):
 
 
 @pytest.mark.parametrize("K,N", [(128, 1), (384, 3), (2048, 300), (8192, 72), (2048, 2)])
-@pytest.mark.parametrize("in_place", [False, True])
-def test_perrow_requant_bit_exact(orc, K, N, in_place):
+@pytest.mark.parametrize("mode", [False, "stride", "compact"])
+def test_perrow_requant_bit_exact(orc, K, N, mode):
     W, _ = workloads.single_gemm(1, K, N, seed=K + N + 1)
     p4 = qg.qg_pack(W.cuda(), 4, group=K)
     ref = orc.requant_4to2(orc.pack(W.numpy(), 4, group=K))
-    tail = p4.codes.view(-1)[N * K // 16:].clone()
-    p2 = qg.qg_requant_4to2(p4, in_place=in_place)
-    _same(p2, ref, f"K={K} N={N} in_place={in_place}")
-    if in_place:
+    before = p4.codes.clone()
+    p2 = (qg.qg_requant_4to2(p4) if not mode else
+          qg.qg_requant_4to2(p4, in_place=True, compact=mode == "compact"))
+    _same(p2, ref, f"K={K} N={N} mode={mode}")
+    if mode:
         assert p2.codes.data_ptr() == p4.codes.data_ptr()
-        assert torch.equal(p4.codes.view(-1)[N * K // 16:], tail), "INT4 tail was touched"
+    if mode == "compact":
+        assert torch.equal(p4.codes.view(-1)[N * K // 16:], before.view(-1)[N * K // 16:]), \
+            "INT4 tail was touched"
+    elif mode == "stride":
+        assert torch.equal(p4.codes[:, K // 16:], before[:, K // 16:]), "back half touched"
 
 
 def test_perrow_requant_rejects_mixed_groups():
