@@ -99,7 +99,13 @@ struct GemvMath {
 
 // LPR lanes cover one row per chunk of 32*LPR codes; CPR chunks per row;
 // 64/LPR rows per wave step; U row steps per wave; K = 32*LPR*CPR is a
-// compile-time constant of each variant.  With LN, the activations are
+// compile-time constant of each variant.  KW > 1 (rows of several chunks
+// per lane, LPR = 64) splits K over KW waves of the workgroup: wave w takes
+// chunks [w' CPR/KW, (w'+1) CPR/KW) (w' = w mod KW) of the same U rows, so
+// each wave loads only its part of the activations (a wave holding whole
+// rows re-reads all K activations per U rows, which for K = 8192 moved more
+// bytes than the codes); the KW wave sums of a row are added in wave order
+// through LDS.  With LN, the activations are
 // fp16(LayerNorm(hln)): the workgroup's 256 threads normalise the row once
 // (mean, then population variance of the centred values, eps 1e-5, reduced
 // by DPP in each wave and then in wave order through LDS), stage it in LDS
@@ -119,7 +125,7 @@ struct GemvWeights {
     SzIdx sz;        // scale addressing, the same for both weights
 };
 
-template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
+template <int BITS, int LPR, int CPR, int KW, int U, bool LN, int NW>
 __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                                               const float* __restrict__ hln,
                                               uint16_t* __restrict__ norm_out,
@@ -131,13 +137,20 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     constexpr int WPL = G::WPL;
     constexpr int PAIRS = G::PAIRS;  // FP16 pairs of x per lane and chunk
     constexpr int K = 32 * LPR * CPR;
+    constexpr int CW = CPR / KW;  // chunks per lane (this wave's part of K)
+    static_assert(KW == 1 || (LPR == 64 && CPR % KW == 0 && KW <= 4 && U <= 64),
+                  "K parts of whole waves");
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wib = threadIdx.x >> 6;  // wave in the workgroup
+    const int kp = wib % KW;           // this wave's K part
+    const int set = blockIdx.x * (4 / KW) + wib / KW;
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
-    const int row0 = wave * U * RPW;
+    const int row0 = set * U * RPW;
+    const int c0 = kp * CW;  // first chunk of the lane
     const bool active = row0 < N;
-    if (!LN && !active) return;  // (LN variants keep every wave for the barriers)
+    // (LN variants and K parts keep every wave for the barriers)
+    if (!LN && KW == 1 && !active) return;
 
     // Load order.  Vector-memory loads of a wave complete in issue order, so
     // the activations (or the LayerNorm input) go first: the arithmetic that
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     // no branch splits the loads into dependent round trips.
     constexpr int VPT = LN ? K / 256 : 4;  // LayerNorm values per thread
     float4 hv[VPT / 4];
-    u32x4 xv[CPR][PAIRS / 4];
+    u32x4 xv[CW][PAIRS / 4];
     if constexpr (LN) {
         static_assert(K % 1024 == 0, "K must be a multiple of 1024 for the fused LayerNorm");
         const float4* hp = (const float4*)(hln + threadIdx.x * VPT);
@@ -156,23 +169,23 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         for (int i = 0; i < VPT / 4; ++i) hv[i] = hp[i];
     } else {
 #pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const u32x4* xp = (const u32x4*)(X + (c * LPR + sub) * 32);
+        for (int c = 0; c < CW; ++c) {
+            const u32x4* xp = (const u32x4*)(X + ((c0 + c) * LPR + sub) * 32);
 #pragma unroll
             for (int v = 0; v < PAIRS / 4; ++v) xv[c][v] = xp[v];
         }
     }
 
-    typename G::Chunk wv[NW][U][CPR];
-    uint16_t sv[NW][U][CPR], zv[NW][U][CPR];
+    typename G::Chunk wv[NW][U][CW];
+    uint16_t sv[NW][U][CW], zv[NW][U][CW];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int row = min(row0 + u * RPW + rsub, N - 1);
 #pragma unroll
         for (int b = 0; b < NW; ++b)
 #pragma unroll
-            for (int c = 0; c < CPR; ++c) {
-                const int wi = (c * LPR + sub) * WPL;
+            for (int c = 0; c < CW; ++c) {
+                const int wi = ((c0 + c) * LPR + sub) * WPL;
                 wv[b][u][c] = *(const typename G::Chunk*)(W.codes[b] + (int64_t)row * W.ldc[b] + wi);
                 const int64_t sg = W.sz.at(row, wi / F::kWordsPerGroup);
                 sv[b][u][c] = W.scales[b][sg];
@@ -181,10 +194,13 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     }
     // The epilogue's own input (the residual element, or the gate output),
     // loaded with the rest so that the store does not wait for a round trip.
-    uint32_t ein[U];
+    // With K parts lane u < U of the part-0 wave stores row u of the set.
+    constexpr int NE = KW == 1 ? U : 1;
+    uint32_t ein[NE];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int row = min(row0 + u * RPW + rsub, N - 1);
+    for (int u = 0; u < NE; ++u) {
+        const int row = KW == 1 ? min(row0 + u * RPW + rsub, N - 1)
+                                : min(row0 + min(lane, U - 1), N - 1);
         ein[u] = NW == 1 ? epi_input(out, 0, row, W.codes[0]) : 0u;
     }
     // Keep the compiler's scheduler from sinking loads into the arithmetic
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     __builtin_amdgcn_sched_barrier(0);
 
     // Activations for this lane's k positions, reused for every row.
-    f16x2 xr[CPR][PAIRS];
+    f16x2 xr[CW][PAIRS];
     if constexpr (LN) {
         // The workgroup's 256 threads normalise the row once: mean, then the
         // population variance of the centred values (eps 1e-5), each reduced
@@ -240,16 +256,16 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
             for (int i = 0; i < VPT / 2; ++i) op[i] = xl[t * (VPT / 2) + i];
         }
         lds_barrier();
-        if (!active) return;
+        if (KW == 1 && !active) return;
 #pragma unroll
-        for (int c = 0; c < CPR; ++c) {
-            const int p0 = (c * LPR + sub) * 16;
+        for (int c = 0; c < CW; ++c) {
+            const int p0 = ((c0 + c) * LPR + sub) * 16;
 #pragma unroll
             for (int i = 0; i < PAIRS; ++i) xr[c][i] = as_f16x2(xl[p0 + i]);
         }
     } else {
 #pragma unroll
-        for (int c = 0; c < CPR; ++c)
+        for (int c = 0; c < CW; ++c)
 #pragma unroll
             for (int v = 0; v < PAIRS / 4; ++v) {
                 xr[c][4 * v + 0] = as_f16x2(xv[c][v].x);
@@ -258,9 +274,9 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                 xr[c][4 * v + 3] = as_f16x2(xv[c][v].w);
             }
     }
-    float xs[CPR][G::NC], xs_all[CPR];
+    float xs[CW][G::NC], xs_all[CW];
 #pragma unroll
-    for (int c = 0; c < CPR; ++c) {
+    for (int c = 0; c < CW; ++c) {
         G::xsums(xr[c], xs[c]);
         xs_all[c] = 0.0f;
 #pragma unroll
@@ -268,6 +284,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     }
 
     const typename G::Consts kc;
+    __shared__ float red[KW > 1 ? 4 : 1][KW > 1 ? U : 1][NW];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc[NW];
@@ -275,7 +292,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
         for (int b = 0; b < NW; ++b) {
             acc[b] = 0.0f;
 #pragma unroll
-            for (int c = 0; c < CPR; ++c) {
+            for (int c = 0; c < CW; ++c) {
                 float a[G::NC];
 #pragma unroll
                 for (int j = 0; j < G::NC; ++j) a[j] = 0.0f;
@@ -284,11 +301,35 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
                 acc[b] += t * (float)as_f16(sv[b][u][c]);
             }
             acc[b] = segment_sum<LPR>(acc[b]);
+            if constexpr (KW > 1) {
+                if (lane == 0) red[wib][u][b] = acc[b];
+            }
         }
         const int row = row0 + u * RPW + rsub;
-        if (sub == 0 && row < N) {
+        if (KW == 1 && sub == 0 && row < N) {
             if constexpr (NW == 1) {
-                epi_store_pre(out, 0, row, acc[0], ein[u]);
+                epi_store_pre(out, 0, row, acc[0], ein[KW == 1 ? u : 0]);
+            } else {
+                const uint16_t g16 = f32_to_f16_bits(acc[0]);
+                gout[row] = g16;
+                out.Y[row] = swiglu_f16(g16, f32_to_f16_bits(acc[1]));
+            }
+        }
+    }
+    if constexpr (KW > 1) {
+        // the K parts of row row0 + lane, summed in part order
+        lds_barrier();
+        const int row = row0 + lane;
+        if (kp == 0 && lane < U && row < N) {
+            float acc[NW];
+#pragma unroll
+            for (int b = 0; b < NW; ++b) {
+                acc[b] = red[wib][lane][b];
+#pragma unroll
+                for (int q = 1; q < KW; ++q) acc[b] += red[wib + q][lane][b];
+            }
+            if constexpr (NW == 1) {
+                epi_store_pre(out, 0, row, acc[0], ein[0]);
             } else {
                 const uint16_t g16 = f32_to_f16_bits(acc[0]);
                 gout[row] = g16;
@@ -325,24 +366,25 @@ GemvShape gemv_shape(int bits, int K) {
 // Rows per wave U: several rows per wave amortise the activations held in
 // registers (and the fused LayerNorm) but cut the number of waves in flight.
 // Measured on MI355X inside the looped block with its weights cache-resident
-// (D = 2048, F = 8192, M = 1): U = 2 from 2048 row steps (QKV, out, up, down,
-// the SwiGLU pair), else U = 1.  U = 4 on the 8192-step FFN projections was
-// even for INT4 and 2-6 % slower per iteration for INT2 and the SwiGLU pair;
-// U = 1 and U = 4 on the 2048-step ones were slower.  At most 8 outstanding
-// code loads per lane (U * CPR * NW <= 8, NW = 2 for the SwiGLU pair).
-template <int BITS, int LPR, int CPR, int U, bool LN, int NW>
+// (D = 2048, F = 8192, M = 1), rows of one chunk per lane: U = 2 from 2048
+// row steps (QKV, out, up, the SwiGLU pair), else U = 1.  U = 4 on the
+// 8192-step FFN projections was even for INT4 and 2-6 % slower per iteration
+// for INT2 and the SwiGLU pair; U = 1 and U = 4 on the 2048-step ones were
+// slower.  At most 8 outstanding code loads per lane (U * CPR/KW * NW <= 8,
+// NW = 2 for the SwiGLU pair).
+template <int BITS, int LPR, int CPR, int KW, int U, bool LN, int NW>
 hipError_t launch_gemv_u(const GemmArgs& a, hipStream_t s) {
-    static_assert(U * CPR * NW <= 8, "at most 8 code loads per lane");
+    static_assert(U * (CPR / KW) * NW <= 8, "at most 8 code loads per lane");
     constexpr int RPW = 64 / LPR;
-    constexpr int kWavesPerBlock = 4;
+    constexpr int kSetsPerBlock = 4 / KW;  // row sets of U * RPW rows
     const int N = a.w->N;
     const int steps = (N + RPW - 1) / RPW;
-    const int waves = (steps + U - 1) / U;
-    const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int sets = (steps + U - 1) / U;
+    const int blocks = (sets + kSetsPerBlock - 1) / kSetsPerBlock;
     const qg_weight* w1 = NW == 2 ? a.w2 : a.w;
     const GemvWeights W{{a.w->codes, w1->codes}, {a.w->scales, w1->scales}, {a.w->zeros, w1->zeros},
                         {code_ld(*a.w), code_ld(*w1)}, sz_idx(*a.w)};
-    k_gemv<BITS, LPR, CPR, U, LN, NW><<<blocks, 64 * kWavesPerBlock, 0, s>>>(
+    k_gemv<BITS, LPR, CPR, KW, U, LN, NW><<<blocks, 256, 0, s>>>(
         a.X, a.ln_h, a.norm_out, W, N, a.out(), a.g_out);
     return hipGetLastError();
 }
@@ -355,27 +397,46 @@ constexpr bool ln_variant_ok() {
     return K % 1024 == 0 && K <= 8192;
 }
 
+// Rows of several chunks per lane (K >= 4096) split K over KW = min(CPR, 4)
+// waves, with U = 8 / (CPR/KW * NW) rows per set (the same code loads per
+// lane as whole rows at U = 2), halved while that leaves fewer than 256
+// workgroups.
+template <int BITS, int LPR, int CPR, bool LN, int NW>
+hipError_t launch_gemv_kparts(const GemmArgs& a, hipStream_t s) {
+    constexpr int KW = CPR < 4 ? CPR : 4;
+    constexpr int UMAX = 8 / (CPR / KW * NW);
+    const int N = a.w->N;
+    auto blocks = [&](int u) { return (N + u * (4 / KW) - 1) / (u * (4 / KW)); };
+    if (blocks(UMAX) >= 256 || UMAX == 1) return launch_gemv_u<BITS, LPR, CPR, KW, UMAX, LN, NW>(a, s);
+    if constexpr (UMAX >= 2) {
+        if (blocks(UMAX / 2) >= 256 || UMAX == 2)
+            return launch_gemv_u<BITS, LPR, CPR, KW, UMAX / 2, LN, NW>(a, s);
+    }
+    if constexpr (UMAX >= 4) {
+        return launch_gemv_u<BITS, LPR, CPR, KW, UMAX / 4, LN, NW>(a, s);
+    }
+    return hipErrorInvalidValue;  // not reached
+}
+
 template <int BITS, int LPR, int CPR, bool LN>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t s) {
     if constexpr (LN && !ln_variant_ok<BITS, LPR, CPR>()) {
         return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_layernorm
+    } else if constexpr (CPR > 1) {
+        if (a.w2 != nullptr) {  // SwiGLU pair: two weights per row
+            if constexpr (CPR <= 4) return launch_gemv_kparts<BITS, LPR, CPR, LN, 2>(a, s);
+            return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_swiglu
+        }
+        return launch_gemv_kparts<BITS, LPR, CPR, LN, 1>(a, s);
     } else {
     constexpr int RPW = 64 / LPR;
     const int steps = (a.w->N + RPW - 1) / RPW;
     if (a.w2 != nullptr) {  // SwiGLU pair: two weights per row step
-        if constexpr (CPR <= 4) {
-            if constexpr (CPR <= 2) {
-                if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 2>(a, s);
-            }
-            return launch_gemv_u<BITS, LPR, CPR, 1, LN, 2>(a, s);
-        } else {
-            return hipErrorInvalidValue;  // never dispatched: see gemm_fuses_swiglu
-        }
+        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 1, 2, LN, 2>(a, s);
+        return launch_gemv_u<BITS, LPR, CPR, 1, 1, LN, 2>(a, s);
     }
-    if constexpr (CPR <= 4) {
-        if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 2, LN, 1>(a, s);
-    }
-    return launch_gemv_u<BITS, LPR, CPR, 1, LN, 1>(a, s);
+    if (steps >= 2 * 1024) return launch_gemv_u<BITS, LPR, CPR, 1, 2, LN, 1>(a, s);
+    return launch_gemv_u<BITS, LPR, CPR, 1, 1, LN, 1>(a, s);
     }
 }
 
