@@ -24,6 +24,15 @@ namespace {
 
 // ------------------------------------------------------ MFMA B fragments ----
 
+// fp16_rne((q - z) s) of codes 2i, 2i+1 of word w: (1024 + q) pairs by one
+// fused mask-and-or (mask in an SGPR, bias in a VGPR), then the exact
+// subtraction of 1024 + z and one rounding of the product.
+template <int BITS>
+__device__ __forceinline__ f16x2 dequant_pair_fused(uint32_t w, int i, const GroupConst& gc,
+                                                    uint32_t mask, uint32_t bias) {
+    return (as_f16x2(((w >> (BITS * i)) & mask) | bias) + gc.nbz) * gc.s2;
+}
+
 // Codes of one 128-k group for one lane (k in [32c, 32c + 32) of row n).
 template <int BITS>
 struct LaneCodes;
@@ -34,10 +43,13 @@ struct LaneCodes<4> {
         w = *(const u32x4*)(row + g * 16 + c * 4);
     }
     // FP16 B fragment of MFMA step j: codes 8j..8j+7 of the lane = word j.
-    __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc) const {
+    __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc, uint32_t mask,
+                                          uint32_t bias) const {
         const uint32_t x = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-        const f16x2 p0 = dequant_pair_f16<4>(x, 0, gc), p1 = dequant_pair_f16<4>(x, 1, gc);
-        const f16x2 p2 = dequant_pair_f16<4>(x, 2, gc), p3 = dequant_pair_f16<4>(x, 3, gc);
+        const f16x2 p0 = dequant_pair_fused<4>(x, 0, gc, mask, bias);
+        const f16x2 p1 = dequant_pair_fused<4>(x, 1, gc, mask, bias);
+        const f16x2 p2 = dequant_pair_fused<4>(x, 2, gc, mask, bias);
+        const f16x2 p3 = dequant_pair_fused<4>(x, 3, gc, mask, bias);
         return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     }
 };
@@ -48,11 +60,14 @@ struct LaneCodes<2> {
         w = *(const u32x2*)(row + g * 8 + c * 2);
     }
     // Step j: codes 8j..8j+7 = pairs 4(j&1)..4(j&1)+3 of word j>>1.
-    __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc) const {
+    __device__ __forceinline__ f16x8 frag(int j, const GroupConst& gc, uint32_t mask,
+                                          uint32_t bias) const {
         const uint32_t x = (j >> 1) ? w.y : w.x;
         const int p = (j & 1) * 4;
-        const f16x2 p0 = dequant_pair_f16<2>(x, p + 0, gc), p1 = dequant_pair_f16<2>(x, p + 1, gc);
-        const f16x2 p2 = dequant_pair_f16<2>(x, p + 2, gc), p3 = dequant_pair_f16<2>(x, p + 3, gc);
+        const f16x2 p0 = dequant_pair_fused<2>(x, p + 0, gc, mask, bias);
+        const f16x2 p1 = dequant_pair_fused<2>(x, p + 1, gc, mask, bias);
+        const f16x2 p2 = dequant_pair_fused<2>(x, p + 2, gc, mask, bias);
+        const f16x2 p3 = dequant_pair_fused<2>(x, p + 3, gc, mask, bias);
         return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     }
 };
@@ -132,16 +147,34 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
     // accumulator rows >= M, which are never stored.
     const i32x4 rx = make_rsrc_sgpr(X, ((int64_t)(M - 1) * ldx + K) * 2);
     const int units = M * cpr;
-    for (int u0 = wave * 64; u0 < units; u0 += 256) {
-        const int u = u0 + lane;
-        const int row = u / cpr, slot = u % cpr;
-        const int ci = slot ^ (row & 15);
-        dma16(rx, xs + u0 * 16, (uint32_t)((row * ldx + (int64_t)gbeg * kGroup + ci * 8) * 2));
+    if (cpr % 64 == 0) {
+        // each instruction's 64 units lie in one row: the row and the run's
+        // first chunk advance by scalar steps (no per-lane division)
+        int row = (wave * 64) / cpr, slot0 = (wave * 64) % cpr;
+        for (int u0 = wave * 64; u0 < units; u0 += 256) {
+            const int ci = (slot0 + lane) ^ (row & 15);
+            dma16(rx, xs + u0 * 16,
+                  (uint32_t)(((int64_t)row * ldx + (int64_t)gbeg * kGroup + ci * 8) * 2));
+            slot0 += 256;
+            while (slot0 >= cpr) {
+                slot0 -= cpr;
+                ++row;
+            }
+        }
+    } else {
+        for (int u0 = wave * 64; u0 < units; u0 += 256) {
+            const int u = u0 + lane;
+            const int row = u / cpr, slot = u % cpr;
+            const int ci = slot ^ (row & 15);
+            dma16(rx, xs + u0 * 16, (uint32_t)((row * ldx + (int64_t)gbeg * kGroup + ci * 8) * 2));
+        }
     }
     wait_vmcnt<0>();
     lds_barrier();
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t pair_mask = sgpr_const(Fmt<BITS>::kPairMask);
+    const uint32_t bias = vgpr_const(kBias2);
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = zero4;
@@ -158,7 +191,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
                 const f16x8 a = *(const f16x8*)(xs + (nl * cpr + (ci ^ nl)) * 16);
                 f16x8 bf[NT];
 #pragma unroll
-                for (int t = 0; t < NT; ++t) bf[t] = lc[t][i].frag(j, gc[t]);
+                for (int t = 0; t < NT; ++t) bf[t] = lc[t][i].frag(j, gc[t], pair_mask, bias);
                 // MFMAs at raised wave priority (two workgroups share a CU:
                 // measured 2-4 % faster, bit-identical)
                 __builtin_amdgcn_s_setprio(1);
