@@ -332,6 +332,189 @@ def trace_from(trace_csv: str, command: str):
     print(json.dumps({k: rec[k] for k in ("decode", "prefill")})[:2000])
 
 
+# Loop workloads of the per-kernel breakdown, in launch order:
+# (name, bits, M, L).
+LOOP_CONFIGS = (("c2_int4_block_m1_l8", 4, 1, 8), ("c4a_int2_block_m1_l16", 2, 1, 16),
+                ("c5a_int4_block_m16_l32", 4, 16, 32), ("c4b_int2_block_m128_l8", 2, 128, 8),
+                ("c3_int4_block_m512_l8", 4, 512, 8))
+LOOPS_JSON = os.path.join(ROOT, "profiles", "loop_kernels.json")
+LOOPS_MD = os.path.join(ROOT, "profiles", "loop_kernels.md")
+
+
+def loops_target(qg, torch, workloads, calls: int = 4):
+    """Trace / counter target: each loop workload of LOOP_CONFIGS packed (its
+    pack kernels mark where it starts in a trace), one warm-up call, then
+    `calls` calls of qg_loop_range."""
+    dev = "cuda"
+    for name, bits, M, L in LOOP_CONFIGS:
+        inp = workloads.block(M, seed=0)
+        blk = qg.pack_block(inp.W, bits, D, F, dev)
+        scratch = qg.alloc_loop_scratch(blk, M, dev)
+        h = inp.X.float().to(dev)
+        torch.cuda.synchronize()
+        for _ in range(1 + calls):
+            qg.qg_loop_range(blk, h, 0, L, scratch)
+        torch.cuda.synchronize()
+        log(f"loops target: {name}: {1 + calls} calls")
+
+
+def loop_pattern(disp, first: int, M: int, end: int | None = None):
+    """Kernel sequence of one loop iteration starting at dispatch `first` of
+    disp = [(signature, value)] (signature = (kernel name, grid...)): the
+    period until the first signature recurs; every exact repetition of it in
+    disp[first:end] is collected, so launches outside the loop do not mix
+    in.  Returns (labels, signatures, per-position value lists, repetitions);
+    labels name the projection of each GEMM launch (qkv, out, up, down) and
+    `projection+kernel` for the launches that finish one."""
+    end = len(disp) if end is None else end
+    sig0 = disp[first][0]
+    period = next(p for p in range(1, end - first) if disp[first + p][0] == sig0)
+    pat = [disp[first + j][0] for j in range(period)]
+    per = [[] for _ in pat]
+    i, reps = first, 0
+    while i + period <= end:
+        if all(disp[i + j][0] == pat[j] for j in range(period)):
+            for j in range(period):
+                per[j].append(disp[i + j][1])
+            i, reps = i + period, reps + 1
+        else:
+            i += 1
+    labels, gi, prev = [], 0, None
+    for sig in pat:
+        name = sig[0]
+        if "k_gemv" in name or "k_gemm" in name:
+            prev = PROJ[gi % len(PROJ)]
+            gi += 1
+            labels.append(prev)
+        else:
+            labels.append(f"{prev}+{name.split('<')[0].split('::')[-1]}")
+    return labels, pat, per, reps
+
+
+def loop_segments(names):
+    """[start, end) dispatch ranges of the LOOP_CONFIGS workloads in a
+    loops-target run: each begins after its weights' pack kernels, and the
+    loop's first iteration begins at its first GEMV (M = 1) or at the first
+    launch after its first LayerNorm (M > 1)."""
+    starts, loop_seen = [], True
+    for i, n in enumerate(names):
+        if "k_pack" in n:
+            if loop_seen:
+                starts.append(i)
+            loop_seen = False
+        elif "k_gemv" in n or "k_gemm" in n or "k_layernorm" in n:
+            loop_seen = True
+    assert len(starts) >= len(LOOP_CONFIGS), f"{len(starts)} pack groups in the trace"
+    starts = starts[-len(LOOP_CONFIGS):]
+    bounds = starts[1:] + [len(names)]
+    segs = []
+    for (name, bits, M, L), a, b in zip(LOOP_CONFIGS, starts, bounds):
+        if M == 1:
+            first = next(i for i in range(a, b) if "k_gemv" in names[i])
+        else:
+            first = next(i for i in range(a, b) if "k_layernorm" in names[i]) + 1
+        segs.append((first, b))
+    return segs
+
+
+def loops_from(trace_csv: str, pmc_csvs, command: str):
+    """profiles/loop_kernels.json and .md: per loop workload of LOOP_CONFIGS,
+    every launch of one iteration with its rocprofv3 kernel-trace duration
+    (median over the matched iterations) and, from `rocprofv3 --pmc` runs of
+    the same target, the median of each SQ counter per launch and the ratios
+    derived from them."""
+    import csv
+    import statistics
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    disp = [((r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"])),
+             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
+    segs = loop_segments([d[0][0] for d in disp])
+    # counters: dispatch -> {counter: value summed over the rows of that dispatch}
+    pmc_disp = []
+    for path in pmc_csvs:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            d = int(r["Dispatch_Id"])
+            e = per.setdefault(d, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        pmc_disp.append([per[d] for d in sorted(per)])
+    rec = {"command": command, "trace": os.path.basename(trace_csv),
+           "counters": [os.path.basename(p) for p in pmc_csvs],
+           "sources_sha256_16": sources_hash(), "configs": {}}
+    for (name, bits, M, L), (first, end) in zip(LOOP_CONFIGS, segs):
+        labels, pat, per, reps = loop_pattern(disp, first, M, end)
+        units = proj_units(M, bits)
+        ks = []
+        for lab, sig, ts in zip(labels, pat, per):
+            e = {"label": lab, "kernel": sig[0].replace("void ", "")
+                 .replace("qg::(anonymous namespace)::", "").split("(")[0], "grid": list(sig[1:]),
+                 "median_us": round(statistics.median(ts), 3), "count": len(ts)}
+            if lab in units:
+                e.update(bytes=units[lab]["bytes"], flop=units[lab]["flop"])
+            ks.append(e)
+        # the same launches in each counter run
+        for pd in pmc_disp:
+            pn = [e["name"] for e in pd]
+            pf, pe = loop_segments(pn)[[c[0] for c in LOOP_CONFIGS].index(name)]
+            pdisp = [((e["name"], e["grid"]), e["c"]) for e in pd]
+            _, _, pper, _ = loop_pattern(pdisp, pf, M, pe)
+            for e, vals in zip(ks, pper):
+                for cn in vals[0]:
+                    e.setdefault("counters", {})[cn] = statistics.median(v[cn] for v in vals)
+        for e in ks:
+            c = e.get("counters", {})
+            d = {}
+            if c.get("SQ_INSTS_MFMA"):
+                d["valu_per_mfma"] = round((c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"])
+                                           / c["SQ_INSTS_MFMA"], 2)
+            if c.get("SQ_WAVE_CYCLES"):
+                d["wait_share"] = round(c.get("SQ_WAIT_INST_ANY", 0) / c["SQ_WAVE_CYCLES"], 3)
+            if c.get("SQ_WAVES"):
+                d["valu_per_wave"] = round(c.get("SQ_INSTS_VALU", 0) / c["SQ_WAVES"], 1)
+            if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                d["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024), 3)
+            if c.get("SQ_LDS_IDX_ACTIVE"):
+                d["lds_bank_conflict_share"] = round(c.get("SQ_LDS_BANK_CONFLICT", 0) / c["SQ_LDS_IDX_ACTIVE"], 3)
+            if d:
+                e["derived"] = d
+        tot = sum(e["median_us"] for e in ks)
+        rec["configs"][name] = {"bits": bits, "M": M, "L": L, "iterations_matched": reps,
+                                "sum_of_medians_us": round(tot, 2), "kernels": ks}
+    with open(LOOPS_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    lines = ["# Per-launch breakdown of the loop workloads (one iteration each)", "",
+             f"commands: `{command}`", "",
+             "Durations are rocprofv3 kernel-trace start-to-end times (median over the matched "
+             "iterations; the trace's own per-dispatch cost makes them slightly longer than the "
+             "graph-timed period); counters are medians per launch over the same iterations of "
+             "separate `--pmc` runs. Derived: VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
+             "SQ_INSTS_MFMA; wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); LDS conflict = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles). "
+             f"Kernel sources sha256/16 = `{rec['sources_sha256_16']}`.", ""]
+    for name, cfg in rec["configs"].items():
+        lines += [f"## {name} (INT{cfg['bits']}, M={cfg['M']}, L={cfg['L']}; "
+                  f"{cfg['iterations_matched']} iterations matched; sum {cfg['sum_of_medians_us']} us)", "",
+                  "| launch | kernel | grid | median us | rate | waves | VALU/wave | VALU/MFMA | wait | MFMA busy | LDS conflict |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for e in cfg["kernels"]:
+            rate = ""
+            if "bytes" in e and cfg["M"] <= 16:
+                rate = f"{e['bytes'] / e['median_us'] / 1e3:.0f} GB/s"
+            elif "flop" in e:
+                rate = f"{e['flop'] / e['median_us'] / 1e6:.0f} TFLOP/s"
+            c, d = e.get("counters", {}), e.get("derived", {})
+            lines.append(f"| {e['label']} | `{e['kernel'][:48]}` | {e['grid']} | {e['median_us']} | {rate} | "
+                         f"{int(c['SQ_WAVES']) if 'SQ_WAVES' in c else ''} | {d.get('valu_per_wave', '')} | "
+                         f"{d.get('valu_per_mfma', '')} | {d.get('wait_share', '')} | {d.get('mfma_busy', '')} | "
+                         f"{d.get('lds_bank_conflict_share', '')} |")
+        lines.append("")
+    with open(LOOPS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v["sum_of_medians_us"] for k, v in rec["configs"].items()}))
+
+
 def trace_record():
     """The committed trace record if it was taken on the current kernel
     sources, else None."""
@@ -680,6 +863,14 @@ def main():
                     help="write profiles/traffic.json from the two counter runs (no GPU)")
     ap.add_argument("--traffic-command", default="",
                     help="the command lines that produced the counter runs, recorded as is")
+    ap.add_argument("--loops-target", action="store_true",
+                    help="only run the loop workloads of the per-launch breakdown (for "
+                         "rocprofv3 --kernel-trace and --pmc runs)")
+    ap.add_argument("--loops-from", nargs="+", metavar="CSV",
+                    help="write profiles/loop_kernels.json and .md from a --kernel-trace CSV of "
+                         "--loops-target, then any --pmc counter CSVs of it (no GPU)")
+    ap.add_argument("--loops-command", default="",
+                    help="the command lines that produced the --loops-from CSVs, recorded as is")
     ap.add_argument("--trace-from", metavar="KERNEL_TRACE_CSV",
                     help="write profiles/roofline_trace.json and .md from a rocprofv3 "
                          "--kernel-trace CSV of this script run with --no-cpu --no-extra (no GPU)")
@@ -692,6 +883,9 @@ def main():
         return
     if args.trace_from:
         trace_from(args.trace_from, args.trace_command)
+        return
+    if args.loops_from:
+        loops_from(args.loops_from[0], args.loops_from[1:], args.loops_command)
         return
 
     if args.gpus != 1:
@@ -712,6 +906,9 @@ def main():
         return
     if args.pmc_prefill:
         pmc_prefill(qg, torch, workloads)
+        return
+    if args.loops_target:
+        loops_target(qg, torch, workloads)
         return
 
     # ---- main leg: INT4 loop block, M=1, L=8 (decode)
