@@ -30,6 +30,11 @@ The JSON line also carries
   * memory: read-only bandwidth of HBM (1 GiB streamed), of the MALL
     (128 MiB, more than the L2s hold) and of the block's 26.7 MB working set
     read back to back (cache-resident);
+  * device: name, CUs, memory, and the shader / memory clock levels sampled
+    from the driver's sysfs files by a second thread while the decode loop
+    runs in an untimed window (the C3 leg carries the same for the prefill
+    loop, with its MFMA fraction at the median shader clock beside the
+    fraction at the 2.4 GHz spec peak);
   * cpu_baseline: the FP64 CPU oracle timed on the host cores on a bounded
     sample of the same workload (whole L=8 steps for ~10 s);
   * extra: the other measured workloads (single-pass INT4 GEMM over a 535 MB
@@ -557,6 +562,88 @@ def memory_ceilings(torch):
                     "read-only; 1024-workgroup grid (2048 for 1 GiB)"}
 
 
+def gpu_clocks(pci: str | None = None):
+    """Current shader (sclk) and memory (mclk) clock levels of the GPU, read
+    from the amdgpu driver's sysfs files (pp_dpm_sclk / pp_dpm_mclk, the
+    level marked '*'), for the card at PCI address `pci` if given, else for
+    every card; with the dense FP16 MFMA peak at that shader clock (256 CUs x
+    4096 FLOP/clk) for comparison with the 2.4 GHz spec peak.  File reads
+    only; an empty dict where the files are not readable."""
+    import glob
+    import re
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            addr = os.path.basename(os.path.realpath(dev))
+            if pci and addr.lower() != pci.lower():
+                continue
+            rec = {}
+            for kind in ("sclk", "mclk"):
+                with open(os.path.join(dev, f"pp_dpm_{kind}")) as f:
+                    cur = [ln for ln in f.read().splitlines() if ln.rstrip().endswith("*")]
+                m = re.search(r"(\d+)\s*Mhz", cur[0], re.I) if cur else None
+                rec[f"{kind}_MHz"] = int(m.group(1)) if m else None
+            if rec.get("sclk_MHz"):
+                rec["mfma_f16_peak_at_sclk_TFLOP/s"] = round(256 * 4096 * rec["sclk_MHz"] / 1e6, 1)
+            out[addr] = rec
+        except (OSError, IndexError):
+            continue
+    if pci and not out:  # address not matched: every card's clocks instead
+        return gpu_clocks(None)
+    return out
+
+
+def sustained_clocks(torch, step, pci, seconds: float = 0.5):
+    """Clock levels sampled every 20 ms by a second thread while the calling
+    thread runs `step` back to back for `seconds` (outside any timed region):
+    the sustained clocks under the workload, as median and range."""
+    import statistics
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            for rec in gpu_clocks(pci).values():
+                samples.append(rec)
+            stop.wait(0.02)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    out = {"samples": len(samples), "steps": n}
+    for k in ("sclk_MHz", "mclk_MHz"):
+        v = [r[k] for r in samples if r.get(k)]
+        if v:
+            out[k] = {"median": statistics.median(v), "min": min(v), "max": max(v)}
+    if "sclk_MHz" in out:
+        out["mfma_f16_peak_at_median_sclk_TFLOP/s"] = round(256 * 4096 * out["sclk_MHz"]["median"] / 1e6, 1)
+    return out
+
+
+def device_pci(torch):
+    """PCI address (dddd:bb:dd.f) of GPU 0 where torch reports it, else None."""
+    p = torch.cuda.get_device_properties(0)
+    if all(hasattr(p, a) for a in ("pci_domain_id", "pci_bus_id", "pci_device_id")):
+        return f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    return None
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1), "pci": device_pci(torch)}
+
+
 def roofline_entries(rec, live_decode, live_prefill, mem):
     """The decode and prefill roofline objects: from the trace record when it
     matches the sources, else from the live HIP-event legs."""
@@ -660,8 +747,16 @@ def c3_leg(qg, torch, workloads):
     reps = int(max(5, min(400, 0.3 / max(t1, 1e-6))))
     per = time_loop(qg, torch, blk, h, L_MAIN, scratch, reps, 2) / reps
     tf = block_flops(512) * L_MAIN / per / 1e12
-    return {"M": 512, "L": L_MAIN, "bits": 4, "calls": reps, "ms_per_call": round(per * 1e3, 4),
-            "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    r = {"M": 512, "L": L_MAIN, "bits": 4, "calls": reps, "ms_per_call": round(per * 1e3, 4),
+         "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    # clock levels under this workload (its own untimed window), and the
+    # fraction against the MFMA peak at the median shader clock seen there
+    clk = sustained_clocks(torch, lambda: qg.qg_loop_range(blk, h, 0, L_MAIN, scratch),
+                           device_pci(torch))
+    r["clocks"] = clk
+    if "mfma_f16_peak_at_median_sclk_TFLOP/s" in clk:
+        r["frac_mfma_at_median_sclk"] = round(tf / clk["mfma_f16_peak_at_median_sclk_TFLOP/s"], 4)
+    return r
 
 
 def extra_legs(qg, torch, workloads, args):
@@ -936,6 +1031,10 @@ def main():
     step_dist = {"unit": "us per step (L=8 iterations), HIP events", "n": len(step_us),
                  "p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90)}
     log(f"step distribution: {step_dist}")
+    # clock levels under the same workload (its own untimed window)
+    clocks = sustained_clocks(torch, lambda: qg.qg_loop_range(blk, h, 0, L_MAIN, scratch),
+                              device_pci(torch))
+    log(f"clocks under the decode loop: {clocks}")
 
     # ---- M=512 chunked prefill (C3): the INT4 block at M=512 rows for L=8;
     # the metric's TFLOP/s leg, and the loop whose kernels the prefill
@@ -1004,6 +1103,7 @@ def main():
         "c3_int4_block_m512_l8": c3,
         "memory": mem,
         "step_distribution": step_dist,
+        "device": dict(device_info(torch), clocks_during_main_workload=clocks),
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

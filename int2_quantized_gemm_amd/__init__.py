@@ -16,7 +16,10 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+# QG_LIBRARY names another build of the same library to load instead of the
+# in-tree one (the host AddressSanitizer build of the CPU test suite); like
+# the in-tree library, it must exist: there is no fallback.
+LIB_PATH = os.environ.get("QG_LIBRARY") or os.path.join(_HERE, "libqgemm.so")
 
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOMEM, QG_EHIP = 0, -1, -2, -3, -4
 GROUP = 128
