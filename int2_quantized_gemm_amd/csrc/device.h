@@ -182,6 +182,52 @@ __device__ __forceinline__ void epi_store(const OutEpi& e, int64_t m, int64_t n,
     if (e.kind == kResidual) e.h[m * e.ldh + n] += (float)as_f16(y);
 }
 
+// Whether the 8-wide epilogue below may use 16-byte accesses for runs of 8
+// outputs n0 .. n0+7 with n0 a multiple of 8: every run lies inside the row
+// (N % 8 == 0) and every operand row starts 16-byte aligned.
+__device__ __forceinline__ bool epi_vec8_ok(const OutEpi& e, int N) {
+    bool ok = N % 8 == 0 && e.ldy % 8 == 0 && ((uintptr_t)e.Y & 15) == 0;
+    if (e.kind == kResidual) ok = ok && e.ldh % 4 == 0 && ((uintptr_t)e.h & 15) == 0;
+    if (e.kind == kGateMul) ok = ok && e.ldg % 8 == 0 && ((uintptr_t)e.g & 15) == 0;
+    return ok;
+}
+
+// The epilogue of outputs (m, n0 .. n0+7) with FP32 accumulators v: the same
+// arithmetic per element as epi_store, with 16-byte loads and stores when vec
+// (epi_vec8_ok); otherwise element by element, skipping columns >= N.
+__device__ __forceinline__ void epi_store8(const OutEpi& e, int64_t m, int n0, int N,
+                                           const float v[8], bool vec) {
+    if (!vec) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (n0 + i < N) epi_store(e, m, n0 + i, v[i]);
+        return;
+    }
+    uint16_t y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = f32_to_f16_bits(v[i]);
+    if (e.kind == kGateMul) {
+        const u32x4 g = *(const u32x4*)(e.g + m * e.ldg + n0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = swiglu_f16((uint16_t)(g[i / 2] >> (16 * (i & 1))), y[i]);
+    }
+    u32x4 yw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yw[i] = (uint32_t)y[2 * i] | ((uint32_t)y[2 * i + 1] << 16);
+    *(u32x4*)(e.Y + m * e.ldy + n0) = yw;
+    if (e.kind == kResidual) {
+        f32x4* hp = (f32x4*)(e.h + m * e.ldh + n0);
+        f32x4 h0 = hp[0], h1 = hp[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h0[i] += (float)as_f16(y[i]);
+            h1[i] += (float)as_f16(y[4 + i]);
+        }
+        hp[0] = h0;
+        hp[1] = h1;
+    }
+}
+
 // The epilogue's input element (h[m][n] as FP32 bits for kResidual, g[m][n]
 // for kGateMul, 0 for kStore), for kernels that load it ahead of their
 // arithmetic; epi_store_pre then finishes exactly like epi_store.  The load is

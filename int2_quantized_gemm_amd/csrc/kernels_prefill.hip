@@ -606,19 +606,52 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         }, std::make_integer_sequence<int, U>{});
     }
 
-    const int n = n0 + col;
-    if (n >= N) return;
+    // Epilogue.  The accumulator layout gives each lane one column and 16
+    // rows; transposed through LDS, each lane holds runs of 8 consecutive
+    // columns of one row instead, so the outputs (and the residual or gate
+    // operands) move in 16-byte accesses rather than 2- and 4-byte ones.
+    // Each wave stages its 32 x 32 FP32 tile in its own 4 KiB of the (then
+    // idle) A ring: element (row, c) at row * 32 + (c ^ 4 (row mod 8)), so
+    // the column-wise writes and the row-wise 16-byte reads spread over the
+    // banks.
+    static_assert(RA * A_BYTES >= 4 * 4096, "epilogue staging fits the A ring");
+    lds_barrier();  // every wave is done reading the ring stages
+    float* st = (float*)&lds_a[0][0] + wave * 1024;
+    const bool vec = part != nullptr ? N % 8 == 0 : epi_vec8_ok(out, N);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = m0 + 32 * tm + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (m >= M) continue;
-            if (part != nullptr)
-                part[(int64_t)blockIdx.z * M * N + (int64_t)m * N + n] = acc[tm][r];
-            else
-                epi_store(out, m, n, acc[tm][r]);
+            const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+            st[row * 32 + (l32 ^ ((row & 7) << 2))] = acc[tm][r];
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = lane + 64 * k;  // run q: row q / 4, columns 8 (q mod 4) + 0..7
+            const int row = q >> 2, c8 = (q & 3) * 8;
+            const int sw = (row & 7) << 2;
+            const f32x4 a = *(const f32x4*)(st + row * 32 + (c8 ^ sw));
+            const f32x4 b = *(const f32x4*)(st + row * 32 + ((c8 + 4) ^ sw));
+            const int m = m0 + 32 * tm + row;
+            const int nn = n0 + wave * 32 + c8;
+            if (m >= M || nn >= N) continue;
+            const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            if (part != nullptr) {
+                float* pp = part + (int64_t)blockIdx.z * M * N + (int64_t)m * N + nn;
+                if (vec) {
+                    ((f32x4*)pp)[0] = a;
+                    ((f32x4*)pp)[1] = b;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (nn + i < N) pp[i] = v[i];
+                }
+            } else {
+                epi_store8(out, m, nn, N, v, vec);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
 
