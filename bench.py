@@ -349,7 +349,10 @@ LOOPS_MD = os.path.join(ROOT, "profiles", "loop_kernels.md")
 def loops_target(qg, torch, workloads, calls: int = 4):
     """Trace / counter target: each loop workload of LOOP_CONFIGS packed (its
     pack kernels mark where it starts in a trace), one warm-up call, then
-    `calls` calls of qg_loop_range."""
+    `calls` calls of qg_loop_range; then two calibration kernels: 13 dense
+    FP16 4096^3 GEMMs of the vendor library (torch.matmul; a known FLOP rate
+    for the MFMA counters) and 20 device copies of COPY_BYTES (known bytes
+    for FETCH_SIZE / WRITE_SIZE)."""
     dev = "cuda"
     for name, bits, M, L in LOOP_CONFIGS:
         inp = workloads.block(M, seed=0)
@@ -361,6 +364,18 @@ def loops_target(qg, torch, workloads, calls: int = 4):
             qg.qg_loop_range(blk, h, 0, L, scratch)
         torch.cuda.synchronize()
         log(f"loops target: {name}: {1 + calls} calls")
+    a = torch.randn(4096, 4096, device=dev, dtype=torch.float16)
+    b = torch.randn(4096, 4096, device=dev, dtype=torch.float16)
+    c = torch.empty(4096, 4096, device=dev, dtype=torch.float16)
+    for _ in range(13):
+        torch.matmul(a, b, out=c)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("loops target: calibration GEMMs and copies done")
 
 
 def loop_pattern(disp, first: int, M: int, end: int | None = None):
@@ -446,6 +461,26 @@ def loops_from(trace_csv: str, pmc_csvs, command: str):
     rec = {"command": command, "trace": os.path.basename(trace_csv),
            "counters": [os.path.basename(p) for p in pmc_csvs],
            "sources_sha256_16": sources_hash(), "configs": {}}
+    # calibration: the copies (bytes) and the dense GEMM (MFMA counters), the
+    # last dispatches of each run
+    scale = {}
+    dense = {}
+    for pd in pmc_disp:
+        copies = [e for e in pd if "copy" in e["name"].lower()]
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [e["c"][cn] for e in copies if cn in e["c"]]
+            if vals:
+                big = max(vals)
+                scale[cn] = COPY_BYTES / (statistics.median(v for v in vals if v > 0.25 * big) * 1024.0)
+        gemm = [e for e in pd if "qg::" not in e["name"] and "copy" not in e["name"].lower()
+                and "fill" not in e["name"].lower()]
+        if gemm:
+            top = max(set(e["name"] for e in gemm), key=lambda n: sum(e["name"] == n for e in gemm))
+            last = [e for e in gemm if e["name"] == top][-10:]
+            dense["kernel"] = top.split("(")[0][:60]
+            for cn in last[0]["c"]:
+                dense.setdefault("counters", {})[cn] = statistics.median(e["c"][cn] for e in last)
+    rec["traffic_scale"] = {k: round(v, 4) for k, v in scale.items()}
     for (name, bits, M, L), (first, end) in zip(LOOP_CONFIGS, segs):
         labels, pat, per, reps = loop_pattern(disp, first, M, end)
         units = proj_units(M, bits)
@@ -469,6 +504,10 @@ def loops_from(trace_csv: str, pmc_csvs, command: str):
         for e in ks:
             c = e.get("counters", {})
             d = {}
+            if "FETCH_SIZE" in c and "FETCH_SIZE" in scale:
+                d["fetch_MB"] = round(c["FETCH_SIZE"] * 1024.0 * scale["FETCH_SIZE"] / 1e6, 3)
+            if "WRITE_SIZE" in c and "WRITE_SIZE" in scale:
+                d["write_MB"] = round(c["WRITE_SIZE"] * 1024.0 * scale["WRITE_SIZE"] / 1e6, 3)
             if c.get("SQ_INSTS_MFMA"):
                 d["valu_per_mfma"] = round((c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"])
                                            / c["SQ_INSTS_MFMA"], 2)
@@ -485,6 +524,17 @@ def loops_from(trace_csv: str, pmc_csvs, command: str):
         tot = sum(e["median_us"] for e in ks)
         rec["configs"][name] = {"bits": bits, "M": M, "L": L, "iterations_matched": reps,
                                 "sum_of_medians_us": round(tot, 2), "kernels": ks}
+    if dense:
+        c = dense["counters"]
+        d = {}
+        if c.get("SQ_INSTS_MFMA"):
+            d["valu_per_mfma"] = round((c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"], 2)
+        if c.get("SQ_WAVE_CYCLES"):
+            d["wait_share"] = round(c.get("SQ_WAIT_INST_ANY", 0) / c["SQ_WAVE_CYCLES"], 3)
+        if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            d["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024), 3)
+        dense["derived"] = d
+        rec["dense_fp16_4096_calibration"] = dense
     with open(LOOPS_JSON, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -496,13 +546,14 @@ def loops_from(trace_csv: str, pmc_csvs, command: str):
              "separate `--pmc` runs. Derived: VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
              "SQ_INSTS_MFMA; wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; MFMA busy = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); LDS conflict = "
-             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles). "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles); fetch / write MB = FETCH_SIZE / "
+             "WRITE_SIZE per launch scaled by the calibration copy. "
              f"Kernel sources sha256/16 = `{rec['sources_sha256_16']}`.", ""]
     for name, cfg in rec["configs"].items():
         lines += [f"## {name} (INT{cfg['bits']}, M={cfg['M']}, L={cfg['L']}; "
                   f"{cfg['iterations_matched']} iterations matched; sum {cfg['sum_of_medians_us']} us)", "",
-                  "| launch | kernel | grid | median us | rate | waves | VALU/wave | VALU/MFMA | wait | MFMA busy | LDS conflict |",
-                  "|---|---|---|---|---|---|---|---|---|---|---|"]
+                  "| launch | kernel | grid | median us | rate | waves | VALU/wave | VALU/MFMA | wait | MFMA busy | LDS conflict | fetch MB | write MB |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for e in cfg["kernels"]:
             rate = ""
             if "bytes" in e and cfg["M"] <= 16:
@@ -513,8 +564,15 @@ def loops_from(trace_csv: str, pmc_csvs, command: str):
             lines.append(f"| {e['label']} | `{e['kernel'][:48]}` | {e['grid']} | {e['median_us']} | {rate} | "
                          f"{int(c['SQ_WAVES']) if 'SQ_WAVES' in c else ''} | {d.get('valu_per_wave', '')} | "
                          f"{d.get('valu_per_mfma', '')} | {d.get('wait_share', '')} | {d.get('mfma_busy', '')} | "
-                         f"{d.get('lds_bank_conflict_share', '')} |")
+                         f"{d.get('lds_bank_conflict_share', '')} | {d.get('fetch_MB', '')} | {d.get('write_MB', '')} |")
         lines.append("")
+    if "dense_fp16_4096_calibration" in rec:
+        dd = rec["dense_fp16_4096_calibration"]
+        lines += ["## Calibration: the vendor library's dense FP16 GEMM, 4096^3 (torch.matmul)", "",
+                  f"`{dd['kernel']}`: " + ", ".join(f"{k} {v}" for k, v in dd["derived"].items()), ""]
+    if scale:
+        lines += [f"Traffic scale factors from the {COPY_BYTES >> 20} MiB device copies (expected bytes / "
+                  f"counted bytes): " + ", ".join(f"{k} x{v:.3f}" for k, v in scale.items()), ""]
     with open(LOOPS_MD, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps({k: v["sum_of_medians_us"] for k, v in rec["configs"].items()}))
