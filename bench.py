@@ -702,6 +702,20 @@ def device_info(torch):
             "memory_GiB": round(p.total_memory / 2**30, 1), "pci": device_pci(torch)}
 
 
+def short_name(kernel: str) -> str:
+    """A kernel's template name without namespaces and parameter list."""
+    return kernel.replace("void ", "").replace("qg::(anonymous namespace)::", "").split("(")[0]
+
+
+def loops_record():
+    """The committed per-launch breakdown (profiles/loop_kernels.json) if it
+    was taken on the current kernel sources, else None."""
+    if not os.path.exists(LOOPS_JSON):
+        return None
+    rec = json.load(open(LOOPS_JSON))
+    return rec if rec.get("sources_sha256_16") == sources_hash() else None
+
+
 def roofline_entries(rec, live_decode, live_prefill, mem):
     """The decode and prefill roofline objects: from the trace record when it
     matches the sources, else from the live HIP-event legs."""
@@ -713,7 +727,8 @@ def roofline_entries(rec, live_decode, live_prefill, mem):
         dec = {"bound": "mall", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(a / HBM_PEAK_GBS, 4),
                "frac_vs_measured_mall_read": round(a / mem["mall_read_128MiB_GB/s"], 4),
-               "kernel": f"{k['kernel'][:60]} ({k['label']} projection, K={k['K']}, N={k['N']}, M=1)",
+               "kernel": f"{short_name(k['kernel'])} ({k['label']} projection, K={k['K']}, N={k['N']}, M=1)",
+               "projection": k["label"],
                "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": k["avg_us"],
                "duration_source": "rocprofv3 kernel trace inside the L=8 loop, "
                                   "profiles/roofline_trace.json / .md",
@@ -723,8 +738,9 @@ def roofline_entries(rec, live_decode, live_prefill, mem):
         t = k["flop"] / k["avg_us"] / 1e6
         pre = {"bound": "mfma", "achieved": round(t, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                "unit": "TFLOP/s", "frac": round(t / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-               "kernel": f"{k['kernel'][:60]} ({k['label']} projection, M=512, K={k['K']}, "
+               "kernel": f"{short_name(k['kernel'])} ({k['label']} projection, M=512, K={k['K']}, "
                          f"N={k['N']})",
+               "projection": k["label"],
                "algorithmic_flop_per_launch": k["flop"], "avg_launch_us": k["avg_us"],
                "duration_source": "rocprofv3 kernel trace inside the L=8 loop, "
                                   "profiles/roofline_trace.json / .md",
@@ -1127,12 +1143,20 @@ def main():
     log(f"memory ceilings: {mem}")
     rec = trace_record()
     roofline, roofline_prefill = roofline_entries(rec, live_decode, live_prefill, mem)
+    # traffic: FETCH_SIZE + WRITE_SIZE per launch of the same kernel, scaled
+    # by the calibration copy, from the committed counter records
     tr = traffic_record()
     roofline["traffic"] = None
-    if tr is not None and rec is not None:
-        lab = roofline["kernel"].split("(")[1].split(" ")[0]
-        if lab in tr["projections"]:
-            roofline["traffic"] = tr["projections"][lab]["hbm_bytes"]
+    if tr is not None and rec is not None and roofline.get("projection") in tr["projections"]:
+        roofline["traffic"] = tr["projections"][roofline["projection"]]["hbm_bytes"]
+        roofline["traffic_source"] = "profiles/traffic.json"
+    lr = loops_record()
+    if lr is not None and rec is not None:
+        for e in lr["configs"]["c3_int4_block_m512_l8"]["kernels"]:
+            d = e.get("derived", {})
+            if e["label"] == roofline_prefill.get("projection") and "fetch_MB" in d and "write_MB" in d:
+                roofline_prefill["traffic"] = int(round((d["fetch_MB"] + d["write_MB"]) * 1e6))
+                roofline_prefill["traffic_source"] = "profiles/loop_kernels.json"
     log(f"roofline: {roofline}")
     log(f"roofline_prefill: {roofline_prefill}")
 
