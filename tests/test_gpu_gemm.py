@@ -57,6 +57,17 @@ def test_gemv_k_variants(orc, bits, K):
 
 
 @pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 1000), (8192, 1536), (8192, 1032),
+                                 (16384, 2048), (16384, 520)])
+def test_gemv_k_parts_row_sets(orc, bits, K, N):
+    """M == 1 with rows of several chunks per lane: K split over the
+    workgroup's waves, every row-set size the launch picks (8, 4, 2 or 1 rows,
+    from how many workgroups N gives), N ragged against the set size."""
+    Y, ref = _case(orc, bits, 1, K, N, seed=K + N + bits)
+    assert_close(Y, ref, f"gemv bits={bits} K={K} N={N}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (1, 2048, 6144), (1, 2048, 8192),
                                    (1, 8192, 2048), (16, 2048, 6144), (16, 8192, 2048),
                                    (128, 2048, 8192), (512, 2048, 2048)])
