@@ -143,7 +143,18 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t* __restrict__ X,
     const int lane = threadIdx.x & 63;
     const int wib = threadIdx.x >> 6;  // wave in the workgroup
     const int kp = wib % KW;           // this wave's K part
-    const int set = blockIdx.x * (4 / KW) + wib / KW;
+    // Workgroup i runs on XCD i mod 8 and each XCD has its own L2: the
+    // launch's first 8 floor(nb / 8) workgroups are renumbered so that each
+    // XCD takes a contiguous eighth of the row blocks (the rest keep their
+    // index).  The loop re-reads the same weights every iteration, and each
+    // XCD then keeps a contiguous share of them in its L2 (measured: the
+    // K = 8192 down projection 3.38 -> 3.25 us, the loop block at M = 1
+    // 1.5-2.6 % faster per iteration, bit-identical).
+    const int nb8 = (int)gridDim.x & ~7;
+    const int blk = (int)blockIdx.x < nb8
+                        ? ((int)blockIdx.x & 7) * (nb8 >> 3) + ((int)blockIdx.x >> 3)
+                        : (int)blockIdx.x;
+    const int set = blk * (4 / KW) + wib / KW;
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
     const int row0 = set * U * RPW;
