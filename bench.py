@@ -21,9 +21,11 @@ The JSON line also carries
     recorded by `rocprofv3 --kernel-trace` in profiles/roofline_trace.json
     (written by --trace-from from a trace of this script; used while the
     kernel sources still hash as recorded), against the 8 TB/s HBM peak and
-    against the measured read bandwidth of the cache the weights live in; the
-    same kernel's HIP-event period over back-to-back graph launches of it on
-    the stream it runs on is reported beside it;
+    against the measured read bandwidths of the L2 (the block read back to
+    back: each XCD's share fits its L2, as in the warm loop; `bound` "l2") and
+    of the MALL; the down-projection GEMV's HIP-event period over
+    back-to-back graph launches of it on the stream it runs on is reported
+    beside it;
   * roofline_prefill: the same for the slowest kernel of the M=512 chunked
     prefill block (C3), in TFLOP/s against the 2516.6 TFLOP/s dense FP16
     MFMA peak;
@@ -724,8 +726,9 @@ def roofline_entries(rec, live_decode, live_prefill, mem):
         gemv = [e for e in rec["decode"]["kernels"] if "bytes" in e]
         k = max(gemv, key=lambda e: e["avg_us"])
         a = k["bytes"] / k["avg_us"] / 1e3
-        dec = {"bound": "mall", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        dec = {"bound": "l2", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(a / HBM_PEAK_GBS, 4),
+               "frac_vs_measured_l2_read": round(a / mem["block_26.7MB_warm_read_GB/s"], 4),
                "frac_vs_measured_mall_read": round(a / mem["mall_read_128MiB_GB/s"], 4),
                "kernel": f"{short_name(k['kernel'])} ({k['label']} projection, K={k['K']}, N={k['N']}, M=1)",
                "projection": k["label"],
@@ -746,8 +749,9 @@ def roofline_entries(rec, live_decode, live_prefill, mem):
                                   "profiles/roofline_trace.json / .md",
                "per_projection_avg_us": {e["label"]: e["avg_us"] for e in rec["prefill"]["kernels"]}}
     else:
-        dec = {"bound": "mall", "achieved": live_decode["GB/s"], "peak": HBM_PEAK_GBS,
+        dec = {"bound": "l2", "achieved": live_decode["GB/s"], "peak": HBM_PEAK_GBS,
                "unit": "GB/s", "frac": round(live_decode["GB/s"] / HBM_PEAK_GBS, 4),
+               "frac_vs_measured_l2_read": round(live_decode["GB/s"] / mem["block_26.7MB_warm_read_GB/s"], 4),
                "frac_vs_measured_mall_read": round(live_decode["GB/s"] / mem["mall_read_128MiB_GB/s"], 4),
                "kernel": live_decode["kernel"], "algorithmic_bytes_per_launch": live_decode["bytes"],
                "avg_launch_us": live_decode["us"],
@@ -895,6 +899,17 @@ def extra_legs(qg, torch, workloads, args):
                                        "frac_hbm": round(blk.nbytes() / cold / 1e9 / HBM_PEAK_GBS, 4),
                                        "method": "graph of 20 L=1 calls on distinct copies, "
                                                  "HIP events over 10 replays"}
+    # Where the warm loop's bytes come from: L=1 calls alternating between two
+    # copies (53.5 MB: MALL-resident, but each copy's per-XCD share has been
+    # displaced from the L2 by the other's) against L=1 calls on one copy.
+    two = graph_leg(torch, lambda i: qg.qg_loop_range(copies[i % 2], h, 0, 1, scratch), 20,
+                    replays=10)
+    one = graph_leg(torch, lambda i: qg.qg_loop_range(copies[0], h, 0, 1, scratch), 20, replays=10)
+    out["c2_int4_block_m1_l2_residency"] = {
+        "us_per_iteration_same_copy": round(one * 1e6, 2),
+        "us_per_iteration_two_copies_alternating": round(two * 1e6, 2),
+        "method": "graphs of 20 L=1 calls, HIP events over 10 replays: the difference is what the "
+                  "L2 saves when the block's per-XCD share stays in it"}
     del copies
     sync()
 
