@@ -254,7 +254,7 @@ def proj_units(M: int, bits: int = 4):
 def trace_from(trace_csv: str, command: str):
     """Per-kernel durations of the decode loop (M=1) and of the M=512 prefill
     loop, from a `rocprofv3 --kernel-trace` CSV of this script (--no-cpu
-    --no-extra).  A loop's kernel sequence is found as the period of
+    --no-extra --no-clocks).  A loop's kernel sequence is found as the period of
     dispatches that starts at its first kernel (the first k_gemv for decode,
     the first kernel after the first k_layernorm for prefill) and every exact
     repetition of it is collected, so launches outside the loops (the live
@@ -814,7 +814,7 @@ def cpu_baseline(budget_s: float):
     }
 
 
-def c3_leg(qg, torch, workloads):
+def c3_leg(qg, torch, workloads, clocks: bool = True):
     """INT4 block at M=512 rows (prefill_chunk = 512), L=8 iterations per
     qg_loop_range call (its cached graph), ~0.3 s of calls after a warm-up."""
     inp = workloads.block(512, seed=0)
@@ -829,6 +829,8 @@ def c3_leg(qg, torch, workloads):
          "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
     # clock levels under this workload (its own untimed window), and the
     # fraction against the MFMA peak at the median shader clock seen there
+    if not clocks:
+        return r
     clk = sustained_clocks(torch, lambda: qg.qg_loop_range(blk, h, 0, L_MAIN, scratch),
                            device_pci(torch))
     r["clocks"] = clk
@@ -1037,6 +1039,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the clock-sampling windows (for kernel-trace runs: their extra "
+                         "iterations, with a sysfs reader beside them, would dominate the trace)")
     ap.add_argument("--pmc-target", action="store_true",
                     help="only launch the roofline kernel and the calibration copy (for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -1057,7 +1062,7 @@ def main():
                     help="the command lines that produced the --loops-from CSVs, recorded as is")
     ap.add_argument("--trace-from", metavar="KERNEL_TRACE_CSV",
                     help="write profiles/roofline_trace.json and .md from a rocprofv3 "
-                         "--kernel-trace CSV of this script run with --no-cpu --no-extra (no GPU)")
+                         "--kernel-trace CSV of this script run with --no-cpu --no-extra --no-clocks (no GPU)")
     ap.add_argument("--trace-command", default="",
                     help="the command line that produced the trace, recorded as is")
     args = ap.parse_args()
@@ -1121,14 +1126,14 @@ def main():
                  "p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90)}
     log(f"step distribution: {step_dist}")
     # clock levels under the same workload (its own untimed window)
-    clocks = sustained_clocks(torch, lambda: qg.qg_loop_range(blk, h, 0, L_MAIN, scratch),
-                              device_pci(torch))
+    clocks = None if args.no_clocks else sustained_clocks(
+        torch, lambda: qg.qg_loop_range(blk, h, 0, L_MAIN, scratch), device_pci(torch))
     log(f"clocks under the decode loop: {clocks}")
 
     # ---- M=512 chunked prefill (C3): the INT4 block at M=512 rows for L=8;
     # the metric's TFLOP/s leg, and the loop whose kernels the prefill
     # roofline is taken from.
-    c3 = c3_leg(qg, torch, workloads)
+    c3 = c3_leg(qg, torch, workloads, clocks=not args.no_clocks)
     log(f"c3: {c3}")
 
     # ---- live legs: the decode roofline kernel's shape (the down-projection
