@@ -308,15 +308,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT) void k_gemm_prefil
 // first step (kSzRegs); per-row groups have one scale and zero per column,
 // loaded once (kSzRow).
 //
-// The four waves each own a 32-column strip of the 128-wide tile (TM = BM/32
-// MFMA tiles of 32 x 32 down it), so a wave dequantises each B fragment once
-// and feeds it to TM MFMAs; that keeps the dequantisation at under 4 VALU
-// instructions per MFMA, which a wave's VALU work still overlaps with its
-// own MFMAs (measured; a 2 x 2 wave grid, which halves the LDS reads but
-// doubles the dequantisation, was slower).  Lane l takes column l % 32 of the
-// strip and the k run [64 h, 64 h + 64) of a step (h = l / 32), slice j the
-// j-th 8 of that run, and reads A fragments with the same assignment, one
-// slice ahead of the MFMAs.
+// Four strips of 32 columns of the 128-wide tile (TM = BM/32 MFMA tiles of
+// 32 x 32 down each), so a strip's B fragments are dequantised once and feed
+// TM MFMAs each; that keeps the dequantisation at under 4 VALU instructions
+// per MFMA, which a wave's VALU work still overlaps with its own MFMAs
+// (measured; a 2 x 2 wave grid, which halves the LDS reads but doubles the
+// dequantisation, was slower).  KS = 1: one wave per strip.  KS = 2: two
+// waves per strip (8 per workgroup), wave 4 s + k taking k-slices 4 k ..
+// 4 k + 3 of every step, so that two waves share each SIMD and one's
+// dequantisation and waits overlap the other's MFMAs; at the end the k = 1
+// wave hands its partial tiles to the k = 0 wave through LDS, which adds them
+// (k = 0 + k = 1) and stores the strip (a different FP32 summation order
+// from KS = 1, within the same tolerance of the oracle).  Measured on MI355X:
+// 64- and 128-row tiles 2-6 % faster on every
+// shape (C5b 80.6 -> 76.5 us, the M = 512 down projection 33.6 -> 31.6 us,
+// C3 -1.4 %, M = 256 block -5 %); 32-row tiles at M <= 128 about 1 % slower,
+// but they too run KS = 2, so that every tile height sums each output in the
+// same order and K split (a GEMM over some of a weight's columns then equals
+// those columns of the whole GEMM bit for bit across tile heights, as the
+// FP16-h cache's K/V rebuild relies on).  Lane l takes column l % 32 of the strip and
+// the k run [64 h, 64 h + 64) of a step (h = l / 32), slice j the j-th 8 of
+// that run, and reads A fragments with the same assignment, one slice ahead
+// of the MFMAs.
 template <int BITS>
 struct RingB {
     static constexpr int CH = BITS == 4 ? 4 : 2;  // 16-byte chunks per column and group
@@ -393,17 +406,26 @@ __device__ __forceinline__ void for_each_index(Fn&& f, std::integer_sequence<int
     (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int BITS, int BM, int RA, int RBS, int SZ>
-__global__ __launch_bounds__(256) void k_gemm_ring(
+template <int BITS, int BM, int RA, int RBS, int SZ, int KS>
+__global__ __launch_bounds__(256 * KS) void k_gemm_ring(
     const uint16_t* __restrict__ X, int64_t ldx, int M, const uint32_t* __restrict__ codes,
     int64_t ldc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int K,
     int N, OutEpi out, int groups_per_part, float* __restrict__ part, Raster rs) {
     using F = Fmt<BITS>;
     using RB = RingB<BITS>;
     constexpr int TM = BM / 32;
+    constexpr int NWV = 4 * KS;                  // waves
     constexpr int A_BYTES = BM * kBK * 2;
-    constexpr int A_DMA = A_BYTES / 1024 / 4;    // A instructions per wave and step
-    constexpr int B_DMA = RB::BYTES / 1024 / 4;  // B instructions per wave and step
+    constexpr int A_INSTR = A_BYTES / 1024;      // A DMA instructions per step
+    constexpr int B_INSTR = RB::BYTES / 1024;    // B DMA instructions per step
+    // per issuing wave and step; the first A_INSTR / A_DMA (B_INSTR / B_DMA)
+    // waves issue them
+    constexpr int A_DMA = A_INSTR >= NWV ? A_INSTR / NWV : 1;
+    constexpr int B_DMA = B_INSTR >= NWV ? B_INSTR / NWV : 1;
+    static_assert(KS == 1 || KS == 2, "k slices of a step split over 1 or 2 waves per strip");
+    static_assert(A_INSTR % NWV == 0 || NWV % A_INSTR == 0, "A DMA over whole waves");
+    static_assert(B_INSTR % NWV == 0 || NWV % B_INSTR == 0, "B DMA over whole waves");
+    constexpr int JB = 8 / KS;                   // k-slices of a step per wave
     constexpr int CH = RB::CH;
     constexpr int LANE_WORDS = 64 / F::kCodesPerWord;  // packed words of a lane's k run
     constexpr int U = RA * RBS / gcd_c(RA, RBS);       // steps per unrolled round
@@ -415,6 +437,11 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int strip = wave & 3;  // 32-column strip of the tile
+    const int ks = wave >> 2;    // which k-slices of a step (KS = 2: slices 4 ks .. 4 ks + 3)
+    const bool a_issuer = wave < A_INSTR / A_DMA;
+    const bool b_issuer = wave < B_INSTR / B_DMA;
+    const int a_n = a_issuer ? A_DMA : 0, b_n = b_issuer ? B_DMA : 0;  // this wave's DMAs per step
     const int l32 = lane & 31, hh = lane >> 5;
     int tx, ty;
     if (!rs.tile(blockIdx.x, tx, ty)) return;  // padding workgroup of the raster
@@ -429,7 +456,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         make_rsrc_sgpr(X + (int64_t)m0 * ldx, ((int64_t)(M - m0 - 1) * ldx + K) * 2);
     const i32x4 rb = make_rsrc_sgpr(codes + (int64_t)n0 * wpr, (int64_t)(N - n0) * wpr * 4);
     // Waves 0, 1 load scales and waves 2, 3 zeros, of columns 64 (w % 2) + lane.
-    const i32x4 rsz = make_rsrc_sgpr((wave < 2 ? scales : zeros) + (int64_t)n0 * groups,
+    const i32x4 rsz = make_rsrc_sgpr((strip < 2 ? scales : zeros) + (int64_t)n0 * groups,
                                      (int64_t)(N - n0) * groups * 2);
 
     // Source offsets of this lane's DMA slots at step 0 of the part.
@@ -449,12 +476,12 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
         const int q = (unit % CH) ^ RB::swz(n);
         b_off[i] = (uint32_t)(n * wpr * 4 + g_lo * F::kWordsPerGroup * 4 + q * 16);
     }
-    const uint32_t sz_off = (uint32_t)((((wave & 1) * 64 + lane) * groups + g_lo) * 2);
+    const uint32_t sz_off = (uint32_t)((((strip & 1) * 64 + lane) * groups + g_lo) * 2);
     // kSzRegs: this lane's column's scales and zeros of the part (G <= 8
     // groups); kSzRow: its column's one scale and zero (groups of K).
     uint16_t sreg[8], zreg[8];
     if constexpr (SZ == kSzRegs) {
-        const int n = n0 + wave * 32 + l32;
+        const int n = n0 + strip * 32 + l32;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const bool ok = i < G && n < N;
@@ -464,27 +491,32 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     }
     GroupConst gc_row{};
     if constexpr (SZ == kSzRow) {
-        const int n = n0 + wave * 32 + l32;
+        const int n = n0 + strip * 32 + l32;
         gc_row = group_const(n < N ? scales[n] : (uint16_t)0, n < N ? zeros[n] : (uint16_t)0);
     }
 
     // Iteration t issues A of step t + RA - 1, then B (and, every 8 steps,
     // the scales and zeros of the next 8) of step t + RB - 1.
+    // (With 8 waves the A and B instructions are spread over the waves that
+    // issue them, and the 4 waves of k-half 0 load the scales and zeros.)
     auto issue = [&](int t) {
         const int sa = t + RA - 1;
-        if (sa >= 0 && sa < G) {
+        if (a_issuer && sa >= 0 && sa < G) {
             uint8_t* dst = lds_a[sa % RA] + wave * A_DMA * 1024;
 #pragma unroll
             for (int i = 0; i < A_DMA; ++i) dma16(ra, dst + i * 1024, a_off[i] + sa * kBK * 2);
         }
         const int sb = t + RBS - 1;
         if (sb >= 0 && sb < G) {
-            uint8_t* dst = lds_b[sb % RBS] + wave * B_DMA * 1024;
+            if (b_issuer) {
+                uint8_t* dst = lds_b[sb % RBS] + wave * B_DMA * 1024;
 #pragma unroll
-            for (int i = 0; i < B_DMA; ++i)
-                dma16(rb, dst + i * 1024, b_off[i] + sb * F::kWordsPerGroup * 4);
-            if (SZ == kSzDma && (sb & 7) == 0)
-                dma16(rsz, &lds_sz[(sb >> 3) & 1][wave >> 1][(wave & 1) * 1024], sz_off + sb * 2);
+                for (int i = 0; i < B_DMA; ++i)
+                    dma16(rb, dst + i * 1024, b_off[i] + sb * F::kWordsPerGroup * 4);
+            }
+            if (SZ == kSzDma && ks == 0 && (sb & 7) == 0)
+                dma16(rsz, &lds_sz[(sb >> 3) & 1][strip >> 1][(strip & 1) * 1024],
+                      sz_off + sb * 2);
         }
     };
 
@@ -497,10 +529,12 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     // Per-lane LDS byte offsets within a stage: the A fragment of slice j for
     // tile row 0 (tile row tm adds 32 rows, 8 KiB), the B codes of this
     // lane's k run, its column's scale and zero.
-    const int col = wave * 32 + l32;  // output channel within the block
-    uint32_t a_lds[8];
+    const int col = strip * 32 + l32;  // output channel within the block
+    const int j0 = ks * JB;             // first k-slice of this wave
+    uint32_t a_lds[JB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a_lds[j] = (uint32_t)((l32 * 16 + ((8 * hh + j) ^ (l32 & 15))) * 16);
+    for (int jj = 0; jj < JB; ++jj)
+        a_lds[jj] = (uint32_t)((l32 * 16 + ((8 * hh + j0 + jj) ^ (l32 & 15))) * 16);
     uint32_t b_lds[LANE_WORDS / 4];
 #pragma unroll
     for (int v = 0; v < LANE_WORDS / 4; ++v)
@@ -524,23 +558,38 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
             gc = group_const(*(const uint16_t*)(Sz + sz_lds),
                              *(const uint16_t*)(Sz + 128 * 16 + sz_lds));
         }
-        uint32_t wd[LANE_WORDS];
+        // the packed words of this wave's slices (all of the lane's k run
+        // with one wave per strip; its half with two)
+        constexpr int WW = JB * 8 / F::kCodesPerWord;
+        uint32_t wd[WW];
+        if constexpr (KS == 1) {
 #pragma unroll
-        for (int v = 0; v < LANE_WORDS / 4; ++v) {
-            const u32x4 t = *(const u32x4*)(Bs + b_lds[v]);
-            wd[4 * v + 0] = t[0];
-            wd[4 * v + 1] = t[1];
-            wd[4 * v + 2] = t[2];
-            wd[4 * v + 3] = t[3];
+            for (int v = 0; v < LANE_WORDS / 4; ++v) {
+                const u32x4 t = *(const u32x4*)(Bs + b_lds[v]);
+                wd[4 * v + 0] = t[0];
+                wd[4 * v + 1] = t[1];
+                wd[4 * v + 2] = t[2];
+                wd[4 * v + 3] = t[3];
+            }
+        } else if constexpr (LANE_WORDS == 8) {  // INT4: words 4 ks .. 4 ks + 3
+            const u32x4 t = *(const u32x4*)(Bs + (ks ? b_lds[1] : b_lds[0]));
+            wd[0] = t[0];
+            wd[1] = t[1];
+            wd[2] = t[2];
+            wd[3] = t[3];
+        } else {  // INT2: words 2 ks, 2 ks + 1
+            const u32x4 t = *(const u32x4*)(Bs + b_lds[0]);
+            wd[0] = ks ? t[2] : t[0];
+            wd[1] = ks ? t[3] : t[1];
         }
         f16x8 a_cur[TM], a_nxt[TM];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) a_cur[tm] = *(const f16x8*)(As + a_lds[0] + tm * 8192);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < JB; ++j) {
             // the next slice's A reads are issued before this slice's MFMAs
             // (the scheduler would otherwise sink each read next to its use)
-            if (j < 7) {
+            if (j < JB - 1) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
                     a_nxt[tm] = *(const f16x8*)(As + a_lds[j + 1] + tm * 8192);
@@ -567,7 +616,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
             for (int tm = 0; tm < TM; ++tm)
                 acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[tm], b, acc[tm], 0, 0, 0);
             __builtin_amdgcn_s_setprio(0);
-            if (j < 7) {
+            if (j < JB - 1) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) a_cur[tm] = a_nxt[tm];
             }
@@ -582,7 +631,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     auto later_ops = [&](int g) {
         const int na = min(g - 1, G - RA) - (g - RA + 2) + 1;
         const int nb = min(g - 1, G - RBS) - (g - RA + 1) + 1;
-        return (na > 0 ? na : 0) * A_DMA + (nb > 0 ? nb : 0) * B_DMA;
+        return (na > 0 ? na : 0) * a_n + (nb > 0 ? nb : 0) * b_n;
     };
 
     for (int t = -(RBS - 1); t < 0; ++t) issue(t);
@@ -614,9 +663,30 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
     // idle) A ring: element (row, c) at row * 32 + (c ^ 4 (row mod 8)), so
     // the column-wise writes and the row-wise 16-byte reads spread over the
     // banks.
-    static_assert(RA * A_BYTES >= 4 * 4096, "epilogue staging fits the A ring");
+    static_assert(RA * A_BYTES >= 4 * TM * 4096, "epilogue staging fits the A ring");
     lds_barrier();  // every wave is done reading the ring stages
-    float* st = (float*)&lds_a[0][0] + wave * 1024;
+    if constexpr (KS == 2) {
+        // the k-half-1 wave of each strip hands its partial tiles to the
+        // k-half-0 wave through the A ring, which adds them (half 0 + half 1)
+        // and stores the strip
+        float* pr = (float*)&lds_a[0][0] + strip * (TM * 1024);
+        if (ks == 1) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pr[(tm * 16 + r) * 64 + lane] = acc[tm][r];
+        }
+        lds_barrier();
+        if (ks == 0) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tm][r] += pr[(tm * 16 + r) * 64 + lane];
+        }
+        lds_barrier();  // partner tiles read before the staging below reuses the ring
+        if (ks == 1) return;
+    }
+    float* st = (float*)&lds_a[0][0] + strip * 1024;
     const bool vec = part != nullptr ? N % 8 == 0 : epi_vec8_ok(out, N);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
@@ -634,7 +704,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(
             const f32x4 a = *(const f32x4*)(st + row * 32 + (c8 ^ sw));
             const f32x4 b = *(const f32x4*)(st + row * 32 + ((c8 + 4) ^ sw));
             const int m = m0 + 32 * tm + row;
-            const int nn = n0 + wave * 32 + c8;
+            const int nn = n0 + strip * 32 + c8;
             if (m >= M || nn >= N) continue;
             const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             if (part != nullptr) {
@@ -803,7 +873,7 @@ hipError_t launch_cfg(const GemmArgs& a, int split, hipStream_t s) {
     return reduce_parts(a, split, part, s);
 }
 
-template <int BITS, int BM, int RA, int RBS, int SZ>
+template <int BITS, int BM, int RA, int RBS, int SZ, int KS = 1>
 hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const int gx = (a.w->N + 127) / 128, gy = (a.M + BM - 1) / BM;
     const double a_bytes = (double)BM * a.w->K * 2 / split;
@@ -811,13 +881,21 @@ hipError_t launch_ring(const GemmArgs& a, int split, hipStream_t s) {
     const Raster rs = make_raster(gx, gy, a_bytes, b_bytes);
     dim3 grid(8 * rs.sx * rs.sy, 1, split);
     float* part = split > 1 || a.parts ? (float*)a.ws : nullptr;
-    k_gemm_ring<BITS, BM, RA, RBS, SZ><<<grid, 256, 0, s>>>(
+    k_gemm_ring<BITS, BM, RA, RBS, SZ, KS><<<grid, 256 * KS, 0, s>>>(
         a.X, a.ldx, a.M, a.w->codes, code_ld(*a.w), a.w->scales, a.w->zeros, a.w->K, a.w->N,
         a.out(), a.w->K / kBK / split, part, rs);
     hipError_t e = hipGetLastError();
     if (a.parts) *a.parts = split;
     if (e != hipSuccess || split == 1 || a.parts) return e;
     return reduce_parts(a, split, part, s);
+}
+
+template <int BITS, int BM, int KS>
+hipError_t launch_ring_sz(const GemmArgs& a, int split, hipStream_t s) {
+    const int sz = ring_sz_mode(a, a.w->K / kBK / split);
+    return sz == kSzRow    ? launch_ring<BITS, BM, 2, 4, kSzRow, KS>(a, split, s)
+           : sz == kSzRegs ? launch_ring<BITS, BM, 2, 4, kSzRegs, KS>(a, split, s)
+                           : launch_ring<BITS, BM, 2, 4, kSzDma, KS>(a, split, s);
 }
 
 template <int BITS>
@@ -830,20 +908,11 @@ hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
         case 2: return launch_cfg<BITS, 64, 64, 2, 2, 1, 1, 0>(a, p.split, s);
         default: break;
     }
-    const int sz = ring_sz_mode(a, a.w->K / kBK / p.split);
-    if (p.cfg == 3) {
-        return sz == kSzRow    ? launch_ring<BITS, 128, 2, 4, kSzRow>(a, p.split, s)
-               : sz == kSzRegs ? launch_ring<BITS, 128, 2, 4, kSzRegs>(a, p.split, s)
-                               : launch_ring<BITS, 128, 2, 4, kSzDma>(a, p.split, s);
-    }
-    if (p.cfg == 5) {
-        return sz == kSzRow    ? launch_ring<BITS, 64, 2, 4, kSzRow>(a, p.split, s)
-               : sz == kSzRegs ? launch_ring<BITS, 64, 2, 4, kSzRegs>(a, p.split, s)
-                               : launch_ring<BITS, 64, 2, 4, kSzDma>(a, p.split, s);
-    }
-    return sz == kSzRow    ? launch_ring<BITS, 32, 2, 4, kSzRow>(a, p.split, s)
-           : sz == kSzRegs ? launch_ring<BITS, 32, 2, 4, kSzRegs>(a, p.split, s)
-                           : launch_ring<BITS, 32, 2, 4, kSzDma>(a, p.split, s);
+    // every tile height on eight waves (two per strip, each half of a
+    // step's k-slices): see k_gemm_ring
+    if (p.cfg == 3) return launch_ring_sz<BITS, 128, 2>(a, p.split, s);
+    if (p.cfg == 5) return launch_ring_sz<BITS, 64, 2>(a, p.split, s);
+    return launch_ring_sz<BITS, 32, 2>(a, p.split, s);
 }
 
 }  // namespace
