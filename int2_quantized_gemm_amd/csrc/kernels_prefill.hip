@@ -665,26 +665,29 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_ring(
     // banks.
     static_assert(RA * A_BYTES >= 4 * TM * 4096, "epilogue staging fits the A ring");
     lds_barrier();  // every wave is done reading the ring stages
-    if constexpr (KS == 2) {
-        // the k-half-1 wave of each strip hands its partial tiles to the
-        // k-half-0 wave through the A ring, which adds them (half 0 + half 1)
-        // and stores the strip
+    if constexpr (KS > 1) {
+        // the k = 1 wave of each strip hands its partial tiles to the k = 0
+        // wave through the A ring, which adds them (k0 + k1) and stores the
+        // strip (written for KS waves per strip, added in k order)
         float* pr = (float*)&lds_a[0][0] + strip * (TM * 1024);
-        if (ks == 1) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
+        for (int kk = 1; kk < KS; ++kk) {
+            if (ks == kk) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pr[(tm * 16 + r) * 64 + lane] = acc[tm][r];
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) pr[(tm * 16 + r) * 64 + lane] = acc[tm][r];
+            }
+            lds_barrier();
+            if (ks == 0) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[tm][r] += pr[(tm * 16 + r) * 64 + lane];
+            }
+            lds_barrier();  // read before the next hand-over (or the staging) reuses the ring
         }
-        lds_barrier();
-        if (ks == 0) {
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[tm][r] += pr[(tm * 16 + r) * 64 + lane];
-        }
-        lds_barrier();  // partner tiles read before the staging below reuses the ring
-        if (ks == 1) return;
+        if (ks != 0) return;
     }
     float* st = (float*)&lds_a[0][0] + strip * 1024;
     const bool vec = part != nullptr ? N % 8 == 0 : epi_vec8_ok(out, N);
