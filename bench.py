@@ -914,6 +914,26 @@ def extra_legs(qg, torch, workloads, args):
                   "L2 saves when the block's per-XCD share stays in it"}
     del copies
     sync()
+    # The same single-pass rate for the INT2 block (40 copies, 535 MB: every
+    # copy again streams from HBM), beside the INT4 one: the INT2/INT4 time
+    # ratio where the weights come from HBM, against the warm loop's.
+    blk2 = qg.pack_block(inp.W, 2, D, F)
+    copies = []
+    for _ in range(40):
+        copies.append(qg.Block(D, F, *(qg.PackedWeight(w.bits, w.K, w.N, w.codes.clone(),
+                                                      w.scales.clone(), w.zeros.clone())
+                                       for w in (blk2.qkv, blk2.out, blk2.up, blk2.down))))
+    scratch2 = qg.alloc_loop_scratch(blk2, 1)
+    cold2 = graph_leg(torch, lambda i: qg.qg_loop_range(copies[i], h, 0, 1, scratch2), len(copies),
+                      replays=5)
+    out["c4a_int2_block_m1_cold_l1"] = {"ms_per_iteration": round(cold2 * 1e3, 4),
+                                        "GB/s": round(blk2.nbytes() / cold2 / 1e9, 1),
+                                        "frac_hbm": round(blk2.nbytes() / cold2 / 1e9 / HBM_PEAK_GBS, 4),
+                                        "int2_over_int4_time": round(cold2 / cold, 3),
+                                        "method": "graph of 40 L=1 calls on distinct copies, "
+                                                  "HIP events over 5 replays"}
+    del copies, blk2, scratch2
+    sync()
 
     loop_case("c4a_int2_block_m1_l16", 2, 1, 16)
     loop_case("c4b_int2_block_m128_l8", 2, 128, 8)
