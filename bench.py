@@ -946,6 +946,47 @@ def extra_legs(qg, torch, workloads, args):
     loop_case("next2_int4_gated_block_m1_l8", 4, 1, 8, gated=True)
     loop_case("next2_int4_gated_block_m512_l8", 4, 512, 8, gated=True)
 
+    # NEXT-4: chunk-first prefill of M = 2048 rows in chunks of 512
+    # (prefill_chunk) through L = 8 iterations with the FP16-h cache written,
+    # against the single-shot M = 2048 loop; and the h cache's K and V rebuild
+    # (one GEMM of the last iteration's cached x, M = 512, on the K and V rows
+    # of the QKV weight).
+    inp = workloads.block(2048, seed=0)
+    blk = qg.pack_block(inp.W, 4, D, F)
+    h = inp.X.float().to(dev)
+    hcache = torch.empty((8, 2048, D), dtype=torch.float16, device=dev)
+    sc = torch.empty(qg.qg_loop_chunked_scratch_bytes(blk, 2048, 512), dtype=torch.uint8,
+                     device=dev)
+
+    def wall(fn, reps):
+        fn()
+        sync()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        sync()
+        return (time.perf_counter() - t0) / reps
+
+    chunked = wall(lambda: qg.qg_loop_range_chunked(blk, h, 0, 8, 512, sc, hcache=hcache), 10)
+    single_scratch = qg.alloc_loop_scratch(blk, 2048)
+    single = wall(lambda: qg.qg_loop_range(blk, h, 0, 8, single_scratch), 10)
+    kv = blk.qkv.rows(D, 3 * D)
+    xk = hcache[7, :512]
+    Ykv = torch.empty(512, 2 * D, dtype=torch.float16, device=dev)
+    rebuild = graph_leg(torch, lambda i: qg.qg_gemm_int4(xk, kv, Y=Ykv), 20, replays=20)
+    flops = block_flops(2048) * 8
+    out["next4_int4_chunked_prefill_m2048_c512_l8"] = {
+        "ms_per_call": round(chunked * 1e3, 4), "TFLOP/s": round(flops / chunked / 1e12, 2),
+        "frac_mfma": round(flops / chunked / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "single_shot_ms_per_call": round(single * 1e3, 4),
+        "single_shot_TFLOP/s": round(flops / single / 1e12, 2),
+        "kv_rebuild_m512_us": round(rebuild * 1e6, 2),
+        "kv_rebuild_TFLOP/s": round(2.0 * 512 * D * 2 * D / rebuild / 1e12, 2),
+        "method": "wall clock over 10 calls after a warm call (chunked, single shot); the K/V "
+                  "rebuild GEMM graph-timed"}
+    del blk, h, hcache, sc, single_scratch, kv, xk, Ykv
+    sync()
+
     # c5b: M=2048 single-shot prefill through the down projection K=8192 -> N=2048.
     W, X = workloads.single_gemm(2048, 8192, 2048, seed=0)
     p = qg.qg_pack(W.to(dev), 4)
